@@ -1,0 +1,12 @@
+"""CPU oracle of block-sparse video attention -- test infrastructure only.
+
+Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py``; the library never imports, links or runs it.  See
+``oracle/reference.py`` for the definitions and the pages they follow.
+"""
+from .reference import *  # noqa: F401,F403
+from .reference import (Geometry, MaskParams, attention, attention_head, block_logits,  # noqa: F401
+                        build_mask, exp_spec, fold_sum, inclusion_probabilities,
+                        philox4x64_10, pool_blocks, sample_uniforms, select_sample,
+                        select_topk, topk_count, score_scale, forward_scale,
+                        log_cluster_table)
