@@ -1,0 +1,202 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = the whole path on one batch: pool Q, pool K, build the mask
+(logits, per-row top-k or sampling, overrides, lists), sparse forward.
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+`value` is the effective throughput of a whole step: forward FLOPs on the
+executed blocks (4 * D * q_block * k_block per selected block) divided by
+the step time.  The forward alone (the dominant kernel) is reported in
+`roofline` and `fwd_*`, timed with HIP events on the launch stream.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd ms/call + effective TFLOP/s (frac of MFMA peak) at 90% sparsity"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan_1p3b_keep10")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-qblocks", type=int, default=48)
+    return ap.parse_args()
+
+
+def _traffic(path_src, name):
+    """HBM bytes per forward launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    f = os.path.join(ROOT, "profiles", f"traffic_fwd_{name}.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    h = hashlib.sha256(open(path_src, "rb").read()).hexdigest()
+    if rec.get("forward_hip_sha256") != h:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, nblocks):
+    """The oracle, as it stands, on one head: pooling and the mask of every
+    row, then token-expanded attention of `nblocks` query blocks."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    g = oracle.Geometry(1, 1, w.text_len, w.frames, w.latent_h, w.latent_w, w.D, w.q_block, w.k_block,
+                        w.seq_alloc)
+    p = oracle.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio, frame0_dense=w.frame0_dense,
+                          text_columns=w.text_columns, log_cluster=w.log_cluster, seed=w.sample_seed)
+    q1, k1, v1 = q[:1, :1], k[:1, :1], v[:1, :1]
+    rng = np.random.default_rng(0)
+    f0 = list(g.frame0_q_blocks())
+    qbl = sorted(set(f0[:max(1, nblocks // 10)]) |
+                 set(rng.choice(g.nqb, nblocks, replace=False).tolist()))[:nblocks]
+    t0 = time.perf_counter()
+    qp = oracle.pool_blocks(q1, g.S, g.q_block)
+    kp = oracle.pool_blocks(k1, g.S, g.k_block)
+    _, cnt, idx, logw = oracle.build_mask(qp, kp, g, p)
+    t1 = time.perf_counter()
+    oracle.attention_head(q1[0, 0], k1[0, 0], v1[0, 0], g, cnt[0, 0], idx[0, 0], logw[0, 0], q_blocks=qbl)
+    t2 = time.perf_counter()
+    flops = 4.0 * w.D * w.q_block * w.k_block * float(cnt[0, 0, qbl].sum())
+    # the sampled q-blocks' share of one head's mask work is charged to them
+    mask_share = (t1 - t0) * len(qbl) / g.nqb
+    sec = (t2 - t1) + mask_share
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0 of {w.name}: pooling + mask of all {g.nqb} rows (charged pro rata) and "
+                      f"float64 token-expanded attention of {len(qbl)} query blocks "
+                      f"({(t2 - t0):.1f} s wall)",
+            "seconds": round(t2 - t0, 2)}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU: the path has no multi-GPU part in this build "
+              f"(asked for --gpus {a.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import block_sparse_attention_42_amd as bsa
+    import workloads as W
+
+    w = W.workload(a.workload)
+    t_gen = time.perf_counter()
+    q, k, v = W.generate(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (torch.from_numpy(x).to(dt).to(dev) for x in (q, k, v))
+    if w.dtype == "bf16":     # what the oracle sees: the bf16 values
+        q, k, v = (t.float().cpu().numpy() for t in (qd, kd, vd))
+    t_gen = time.perf_counter() - t_gen
+    g = bsa.Geometry(w.B, w.H, w.text_len, w.frames, w.latent_h, w.latent_w, w.D, w.q_block, w.k_block,
+                     w.seq_alloc)
+    p = bsa.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio, frame0_dense=w.frame0_dense,
+                       text_columns=w.text_columns, log_cluster=w.log_cluster, seed=w.sample_seed)
+    d = bsa.bsa_derive(g, p)
+    nqb, nkb = d["nqb"], d["nkb"]
+    qp = torch.empty((w.B, w.H, nqb, w.D), dtype=torch.float32, device=dev)
+    kp = torch.empty((w.B, w.H, nkb, w.D), dtype=torch.float32, device=dev)
+    mask = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.uint8, device=dev)
+    cnt = torch.empty((w.B, w.H, nqb), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.int32, device=dev)
+    logw = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.float32, device=dev) if w.mode == "sample" else None
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def step(times=None):
+        e = [ev() for _ in range(4)] if times is not None else None
+        if e: e[0].record(stream)
+        bsa.bsa_pool_blocks(qd, g, g.q_block, out=qp)
+        bsa.bsa_pool_blocks(kd, g, g.k_block, out=kp)
+        if e: e[1].record(stream)
+        bsa.bsa_build_mask(qp, kp, g, p, out=(mask, cnt, idx, logw))
+        if e: e[2].record(stream)
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, out=out)
+        if e:
+            e[3].record(stream)
+            times.append(e)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    blocks = int(cnt.sum().item())
+    flops = 4.0 * w.D * w.q_block * w.k_block * blocks
+
+    # whole steps, bracketed by synchronize on both sides
+    times = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s0 = ev()
+    s0.record(stream)
+    for _ in range(a.steps):
+        step(times)
+    s1 = ev()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = s0.elapsed_time(s1) / a.steps
+    pool_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in times]))
+    mask_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in times]))
+    fwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in times]))
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    pool_bytes = 2 * w.B * w.H * w.S * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (nqb + nkb) * w.D * 4
+
+    traffic = _traffic(os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", "forward.hip"), w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded clustered Q/K, V ~ N(0,1); stands in for Wan2.1 activations)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "head_dim": w.D, "seq_len": w.S,
+                   "seq_alloc": w.seq_alloc, "q_block": w.q_block, "k_block": w.k_block,
+                   "selection": w.mode, "keep_ratio": w.keep_ratio, "frame0_dense": w.frame0_dense,
+                   "text_columns": w.text_columns},
+        "fwd_ms_per_call": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "pool_ms": round(pool_ms, 4),
+        "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+        "mask_ms": round(mask_ms, 4),
+        "executed_blocks": blocks,
+        "density": round(blocks / (w.B * w.H * nqb * nkb), 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(fwd_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks)
+    res["input_gen_s"] = round(t_gen, 1)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Block-sparse self-attention for video diffusion transformers on MI355X (gfx950).
+
+Thin Python binding of ``libbsa.so`` (C ABI in ``include/bsa.h``).  The
+functions keep the C names and only marshal arguments: they check tensor
+shapes, dtypes and devices, allocate outputs with PyTorch when none are
+given, and pass raw device pointers plus the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback.
+
+    g = Geometry(B, H, text_len, frames, latent_h, latent_w, head_dim,
+                 q_block, k_block, seq_alloc)
+    qp = bsa_pool_blocks(q, g, g.q_block)
+    kp = bsa_pool_blocks(k, g, g.k_block)
+    mask, cnt, idx, logw = bsa_build_mask(qp, kp, g, MaskParams(keep_ratio=0.1))
+    out, lse = bsa_forward(q, k, v, g, cnt, idx, logw)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import BsaError
+
+__all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
+           "bsa_build_mask", "bsa_forward", "library_path"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    B: int
+    H: int
+    text_len: int
+    frames: int
+    latent_h: int
+    latent_w: int
+    head_dim: int
+    q_block: int
+    k_block: int
+    seq_alloc: int
+
+    def c(self) -> _lib.bsa_geometry:
+        return _lib.bsa_geometry(self.B, self.H, self.text_len, self.frames, self.latent_h,
+                                 self.latent_w, self.head_dim, self.q_block, self.k_block, 0,
+                                 self.seq_alloc)
+
+
+@dataclasses.dataclass(frozen=True)
+class MaskParams:
+    mode: str = "topk"            # "topk" or "sample"
+    topk: int = 0
+    keep_ratio: float = 0.1
+    frame0_dense: bool = True
+    text_columns: bool = False
+    log_cluster: bool = False
+    seed: int = 0
+
+    def c(self) -> _lib.bsa_mask_params:
+        mode = {"topk": _lib.BSA_SELECT_TOPK, "sample": _lib.BSA_SELECT_SAMPLE}[self.mode]
+        return _lib.bsa_mask_params(mode, self.topk, float(self.keep_ratio), int(self.frame0_dense),
+                                    int(self.text_columns), int(self.log_cluster), 0,
+                                    int(self.seed) & (2 ** 64 - 1))
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.BSA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.BSA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def bsa_derive(g: Geometry, p: Optional[MaskParams] = None) -> dict:
+    """S, nqb, nkb, frame-0 query blocks, last text key block, k and E (host only)."""
+    out = _lib.bsa_derived()
+    pc = p.c() if p is not None else None
+    _lib.check(_lib.lib().bsa_derive(ctypes.byref(g.c()), ctypes.byref(pc) if pc is not None else None,
+                                     ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in _lib.bsa_derived._fields_ if f != "reserved"}
+
+
+def bsa_pool_blocks(x: torch.Tensor, g: Geometry, block: int, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Per-block mean of the valid rows of x [B,H,seq_alloc,D] -> float32 [B,H,ceil(S/block),D]."""
+    d = bsa_derive(g)
+    nb = -(-d["S"] // block)
+    _need(x, "x", (g.B, g.H, g.seq_alloc, g.head_dim))
+    if out is None:
+        out = torch.empty((g.B, g.H, nb, g.head_dim), dtype=torch.float32, device=x.device)
+    _need(out, "out", (g.B, g.H, nb, g.head_dim), torch.float32, x.device)
+    _lib.check(_lib.lib().bsa_pool_blocks(_ptr(x), _dtype_code(x), ctypes.byref(g.c()), block,
+                                          _ptr(out), _stream(stream)))
+    return out
+
+
+def bsa_build_mask(q_pooled: torch.Tensor, k_pooled: torch.Tensor, g: Geometry, p: MaskParams,
+                   want_mask: bool = True, want_logw: Optional[bool] = None, out=None, stream=None):
+    """Block logits -> selection -> overrides -> compacted lists.
+
+    Returns (mask u8 [B,H,nqb,nkb] or None, kv_cnt i32 [B,H,nqb],
+    kv_idx i32 [B,H,nqb,nkb], log_w f32 [B,H,nqb,nkb] or None).  ``out`` may
+    hold preallocated (mask, cnt, idx, logw) tensors.
+    """
+    d = bsa_derive(g, p)
+    nqb, nkb = d["nqb"], d["nkb"]
+    dev = q_pooled.device
+    _need(q_pooled, "q_pooled", (g.B, g.H, nqb, g.head_dim), torch.float32)
+    _need(k_pooled, "k_pooled", (g.B, g.H, nkb, g.head_dim), torch.float32, dev)
+    if want_logw is None:
+        want_logw = p.mode == "sample"
+    if out is None:
+        mask = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
+        cnt = torch.empty((g.B, g.H, nqb), dtype=torch.int32, device=dev)
+        idx = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.int32, device=dev)
+        logw = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.float32, device=dev) if want_logw else None
+    else:
+        mask, cnt, idx, logw = out
+    if mask is not None:
+        _need(mask, "mask", (g.B, g.H, nqb, nkb), torch.uint8, dev)
+    _need(cnt, "kv_cnt", (g.B, g.H, nqb), torch.int32, dev)
+    _need(idx, "kv_idx", (g.B, g.H, nqb, nkb), torch.int32, dev)
+    if logw is not None:
+        _need(logw, "log_w", (g.B, g.H, nqb, nkb), torch.float32, dev)
+    _lib.check(_lib.lib().bsa_build_mask(_ptr(q_pooled), _ptr(k_pooled), ctypes.byref(g.c()),
+                                         ctypes.byref(p.c()), _ptr(mask), _ptr(cnt), _ptr(idx),
+                                         _ptr(logw), _stream(stream)))
+    return mask, cnt, idx, logw
+
+
+def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
+                kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
+                softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+    """Attention of every query block over its listed key blocks.  Returns (out, lse or None)."""
+    d = bsa_derive(g)
+    nqb, nkb = d["nqb"], d["nkb"]
+    shape = (g.B, g.H, g.seq_alloc, g.head_dim)
+    _need(q, "q", shape)
+    dev = q.device
+    _need(k, "k", shape, q.dtype, dev)
+    _need(v, "v", shape, q.dtype, dev)
+    _need(kv_cnt, "kv_cnt", (g.B, g.H, nqb), torch.int32, dev)
+    _need(kv_idx, "kv_idx", (g.B, g.H, nqb, nkb), torch.int32, dev)
+    if log_w is not None:
+        _need(log_w, "log_w", (g.B, g.H, nqb, nkb), torch.float32, dev)
+    if out is None:
+        out = torch.empty(shape, dtype=q.dtype, device=dev)
+    _need(out, "out", shape, q.dtype, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((g.B, g.H, g.seq_alloc), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (g.B, g.H, g.seq_alloc), torch.float32, dev)
+    _lib.check(_lib.lib().bsa_forward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()),
+                                      _ptr(kv_cnt), _ptr(kv_idx), _ptr(log_w),
+                                      ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse),
+                                      _stream(stream)))
+    return out, lse

@@ -1,0 +1,56 @@
+"""Compile libbsa.so (gfx950) in-tree with hipcc.
+
+``python -m block_sparse_attention_42_amd.build`` (or ``build()``) always
+recompiles every source; object files go to ``_build/`` next to this file.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libbsa.so")
+OBJ = os.path.join(HERE, "_build")
+ARCH = "gfx950"
+
+SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "forward.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed fp32 instructions are switched off for every device pass.
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Pooling and mask decisions follow a written-out float32 operation order:
+# no contraction into fused multiply-adds anywhere in those files.
+EXTRA = {"pool.hip": ["-ffp-contract=off"], "mask.hip": ["-ffp-contract=off"],
+         "abi.cpp": ["-x", "hip", "-ffp-contract=off"]}
+
+
+def _compile(src):
+    obj = os.path.join(OBJ, src + ".o")
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in r.stderr.splitlines() if "is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
+    return obj
+
+
+def build(verbose=False):
+    os.makedirs(OBJ, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,256 @@
+// Host side of the C ABI declared in include/bsa.h: argument validation,
+// derived geometry and kernel dispatch.  Every check runs before any launch,
+// so a non-OK status means nothing was enqueued.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bsa_status fail(bsa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bsa_status fail(bsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bsa_status ok() {
+  g_last_error.clear();
+  return BSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Derived {
+  int64_t S;
+  int32_t nqb, nkb;
+  int32_t f0_first, f0_last;
+  int32_t text_last;
+};
+
+// Geometry checks shared by every entry point.
+bsa_status check_geometry(const bsa_geometry* g, Derived* d) {
+  if (!g) return fail(BSA_ERR_INVALID_ARGUMENT, "geometry is NULL");
+  if (g->B < 1 || g->H < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B=%d and H=%d must be >= 1", g->B, g->H);
+  if (g->text_len < 0 || g->frames < 0 || g->latent_h < 0 || g->latent_w < 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "text_len, frames, latent_h, latent_w must be >= 0");
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", g->head_dim);
+  if (g->q_block != 32 && g->q_block != 64)
+    return fail(BSA_ERR_UNSUPPORTED, "q_block %d unsupported (32 or 64)", g->q_block);
+  if (g->k_block != 16 && g->k_block != 32 && g->k_block != 64)
+    return fail(BSA_ERR_UNSUPPORTED, "k_block %d unsupported (16, 32 or 64)", g->k_block);
+  const int64_t S = (int64_t)g->text_len + (int64_t)g->frames * g->latent_h * g->latent_w;
+  if (S < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "sequence is empty (S = %lld)", (long long)S);
+  const int64_t nqb = (S + g->q_block - 1) / g->q_block;
+  const int64_t nkb = (S + g->k_block - 1) / g->k_block;
+  if (nqb > (1 << 30) || nkb > (1 << 30)) return fail(BSA_ERR_UNSUPPORTED, "sequence too long");
+  const int64_t need = std::max(nqb * g->q_block, nkb * g->k_block);
+  if (g->seq_alloc < need)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "seq_alloc %lld < %lld (blocks of the padded sequence)",
+                (long long)g->seq_alloc, (long long)need);
+  if ((int64_t)g->B * g->H > (1 << 24)) return fail(BSA_ERR_UNSUPPORTED, "B*H too large");
+  d->S = S;
+  d->nqb = (int32_t)nqb;
+  d->nkb = (int32_t)nkb;
+  // frame-0 query blocks: frame-0 page, sec. 4
+  if (g->frames > 0 && g->latent_h * g->latent_w > 0) {
+    const int64_t start = g->text_len;
+    const int64_t end = start + (int64_t)g->latent_h * g->latent_w;
+    d->f0_first = (int32_t)(start / g->q_block);
+    d->f0_last = (int32_t)((end - 1) / g->q_block);
+  } else {
+    d->f0_first = d->f0_last = -1;
+  }
+  d->text_last = g->text_len > 0 ? (int32_t)((g->text_len - 1) / g->k_block) : -1;
+  return BSA_OK;
+}
+
+int32_t topk_of(const bsa_mask_params* p, int32_t nkb) {
+  if (p->topk > 0) return p->topk < nkb ? p->topk : nkb;
+  double k = std::ceil(p->keep_ratio * (double)nkb);
+  if (k < 1) k = 1;
+  if (k > nkb) k = nkb;
+  return (int32_t)k;
+}
+
+bsa_status check_params(const bsa_mask_params* p, const Derived& d) {
+  if (!p) return fail(BSA_ERR_INVALID_ARGUMENT, "mask params are NULL");
+  if (p->mode != BSA_SELECT_TOPK && p->mode != BSA_SELECT_SAMPLE)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown selection mode %d", p->mode);
+  if (p->topk < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "topk %d < 0", p->topk);
+  const bool ratio_used = p->mode == BSA_SELECT_SAMPLE || p->topk == 0;
+  if (ratio_used && !(std::isfinite(p->keep_ratio) && p->keep_ratio > 0.0 && p->keep_ratio <= 1.0))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "keep_ratio %g must be in (0, 1]", p->keep_ratio);
+  (void)d;
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+const char* bsa_status_string(int32_t s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported";
+    case BSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error(void) { return g_last_error.c_str(); }
+
+bsa_status bsa_derive(const bsa_geometry* g, const bsa_mask_params* p, bsa_derived* out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARGUMENT, "out is NULL");
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  std::memset(out, 0, sizeof *out);
+  out->S = d.S;
+  out->nqb = d.nqb;
+  out->nkb = d.nkb;
+  out->frame0_first = d.f0_first;
+  out->frame0_last = d.f0_last;
+  out->text_last = d.text_last;
+  if (p) {
+    s = check_params(p, d);
+    if (s != BSA_OK) return s;
+    out->topk = topk_of(p, d.nkb);
+    out->expected = (float)(p->keep_ratio * (double)d.nkb);
+  }
+  return ok();
+}
+
+bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, int32_t block,
+                           float* pooled, void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (dtype != BSA_DTYPE_BF16 && dtype != BSA_DTYPE_F32)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (block != g->q_block && block != g->k_block)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "block %d is neither q_block nor k_block", block);
+  if (!x || !pooled) return fail(BSA_ERR_INVALID_ARGUMENT, "x and pooled must not be NULL");
+  if (!aligned16(x) || !aligned16(pooled))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "x and pooled must be 16-byte aligned");
+  bsa::PoolArgs a;
+  a.x = x;
+  a.out = pooled;
+  a.seq_alloc = g->seq_alloc;
+  a.S = d.S;
+  a.BH = g->B * g->H;
+  a.D = g->head_dim;
+  a.block = block;
+  a.nb = (int32_t)((d.S + block - 1) / block);
+  hipError_t e = bsa::launch_pool(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bsa_geometry* g,
+                          const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
+                          int32_t* kv_idx, float* log_w, void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  s = check_params(p, d);
+  if (s != BSA_OK) return s;
+  if (!q_pooled || !k_pooled || !kv_cnt || !kv_idx)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q_pooled, k_pooled, kv_cnt and kv_idx must not be NULL");
+  if (!aligned16(q_pooled) || !aligned16(k_pooled) || !aligned16(kv_cnt) || !aligned16(kv_idx) ||
+      (mask && !aligned16(mask)) || (log_w && !aligned16(log_w)))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (p->mode == BSA_SELECT_SAMPLE && !log_w)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "sampling needs log_w");
+  const int32_t nkb_max = p->mode == BSA_SELECT_SAMPLE ? 2048 : 8192;
+  if (d.nkb > nkb_max)
+    return fail(BSA_ERR_UNSUPPORTED, "nkb %d > %d for this selection mode", d.nkb, nkb_max);
+  bsa::MaskArgs a;
+  a.qp = q_pooled;
+  a.kp = k_pooled;
+  a.mask = mask;
+  a.cnt = kv_cnt;
+  a.idx = kv_idx;
+  a.logw = log_w;
+  a.H = g->H;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.D = g->head_dim;
+  int rows = 32768 / d.nkb;
+  a.rows_per_group = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
+  a.mode = p->mode;
+  a.topk = topk_of(p, d.nkb);
+  a.expected = (float)(p->keep_ratio * (double)d.nkb);
+  a.scale = (float)(1.0 / std::sqrt((double)g->head_dim));
+  a.log_cluster = p->log_cluster ? 1 : 0;
+  const int64_t n_last = d.S - (int64_t)(d.nkb - 1) * g->k_block;
+  a.ln_full = (float)std::log((double)g->k_block);
+  a.ln_last = (float)std::log((double)n_last);
+  a.frame0_first = p->frame0_dense ? d.f0_first : -1;
+  a.frame0_last = p->frame0_dense ? d.f0_last : -1;
+  a.text_last = p->text_columns ? d.text_last : -1;
+  a.seed = p->seed;
+  hipError_t e = bsa::launch_mask(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtype,
+                       const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                       const float* log_w, float softmax_scale, void* out, float* lse,
+                       void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (dtype != BSA_DTYPE_BF16 && dtype != BSA_DTYPE_F32)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (!q || !k || !v || !kv_cnt || !kv_idx || !out)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, kv_cnt, kv_idx and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(kv_cnt) ||
+      !aligned16(kv_idx) || (log_w && !aligned16(log_w)) || (lse && !aligned16(lse)))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  const int64_t units = (int64_t)g->B * g->H * d.nqb;
+  if (units > 0x7fffffffLL) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+  bsa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cnt = kv_cnt;
+  a.idx = kv_idx;
+  a.logw = log_w;
+  a.out = out;
+  a.lse = lse;
+  a.seq_alloc = g->seq_alloc;
+  a.S = d.S;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.q_block = g->q_block;
+  a.k_block = g->k_block;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)g->head_dim));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = bsa::launch_forward(a, dtype, g->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

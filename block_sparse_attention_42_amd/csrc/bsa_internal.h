@@ -1,0 +1,66 @@
+// Internal declarations shared by the host entry points (abi.cpp) and the
+// gfx950 kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// bfloat16 storage element (bit pattern only; arithmetic is done in float32).
+struct bf16_t {
+  uint16_t bits;
+};
+
+// Launch arguments of the pooling kernel.
+struct PoolArgs {
+  const void* x;      // [BH, seq_alloc, D]
+  float* out;         // [BH, nb, D]
+  int64_t seq_alloc;
+  int64_t S;
+  int32_t BH, D, block, nb;
+};
+
+// Launch arguments of the mask kernel.
+struct MaskArgs {
+  const float* qp;    // [BH, nqb, D]
+  const float* kp;    // [BH, nkb, D]
+  uint8_t* mask;      // [BH, nqb, nkb] or null
+  int32_t* cnt;       // [BH, nqb]
+  int32_t* idx;       // [BH, nqb, nkb]
+  float* logw;        // [BH, nqb, nkb] or null
+  int32_t H, BH, nqb, nkb, D;
+  int32_t rows_per_group;
+  int32_t mode;       // 0 top-k, 1 sample
+  int32_t topk;
+  float expected;
+  float scale;        // fp32(1/sqrt(D))
+  int32_t log_cluster;
+  float ln_full;      // fp32(ln k_block)
+  float ln_last;      // fp32(ln n_last)
+  int32_t frame0_first, frame0_last;   // -1 if off
+  int32_t text_last;                   // -1 if off
+  uint64_t seed;
+};
+
+// Launch arguments of the sparse forward kernel.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cnt;
+  const int32_t* idx;
+  const float* logw;  // or null
+  void* out;
+  float* lse;         // or null
+  int64_t seq_alloc;
+  int64_t S;
+  int32_t BH, nqb, nkb, q_block, k_block;
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
+hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace bsa

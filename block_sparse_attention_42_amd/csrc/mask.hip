@@ -1,0 +1,353 @@
+// Block logits, per-row selection, overrides and compaction on gfx950.
+//
+// Pages: "Attention matrix view: make only frame-0 query rows dense"
+// (sec. 4 override formula, sec. 6 top-k first then frame-0 rows
+// overwritten, sec. 7 text blocks always kept); "Competition Domains Matter
+// ... (EG-Sparse)" (Eq. 2 cluster-size-weighted centroid softmax, the
+// one-key-per-row safeguard); "AB-Attention" (TL;DR: blocks sampled in
+// proportion to importance, reweighted by inverse inclusion probability).
+//
+// One workgroup (8 waves) takes R consecutive query blocks of one head:
+//   A. all 512 threads compute the R x nkb float32 logits into LDS, each
+//      logit as a sequential non-fused multiply-add chain over D in
+//      ascending order (the library's contract, so the integer decisions
+//      that follow are bit-reproducible);
+//   B. each wave then owns one row at a time: radix select of the k-th
+//      largest logit (four 8-bit passes over a per-wave LDS histogram) and a
+//      ballot-ordered compaction for top-k; or exp / water-filling /
+//      Philox draws / log-weights for sampling.  Frame-0 rows skip straight
+//      to "all blocks"; text columns are OR-ed in.
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kMaskThreads = 512;
+constexpr int kMaskWaves = kMaskThreads / 64;
+constexpr int kMaxRows = 16;
+constexpr int kZFloats = 32768;          // LDS logits budget: rows * nkb <= 32768
+constexpr int kMaxPerLane = 32;          // sampling: nkb <= 64 * 32
+
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t order_key(float z) {
+  const uint32_t u = __float_as_uint(z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+// ---- e^t for t <= 0, float32, fixed operation sequence ----------------------
+// Cody & Waite argument reduction (W. J. Cody, W. Waite, "Software Manual for
+// the Elementary Functions", 1980): n = round(t*log2 e), x = t - n*ln2 with
+// ln2 split into a 15-bit high part (n*ln2_hi exact) and a low part; e^x by
+// the degree-7 Taylor polynomial (Horner, no fused multiply-add); result
+// r * 2^n.  Arguments with t*log2 e < -125 give 0.
+__device__ __forceinline__ float exp_le0(float t) {
+  const float kLog2e = (float)1.4426950408889634;
+  const float kLn2Hi = (float)0.693145751953125;
+  const float kLn2Lo = (float)(0.6931471805599453 - 0.693145751953125);
+  const float c0 = (float)(1.0 / 1.0), c1 = (float)(1.0 / 1.0), c2 = (float)(1.0 / 2.0);
+  const float c3 = (float)(1.0 / 6.0), c4 = (float)(1.0 / 24.0), c5 = (float)(1.0 / 120.0);
+  const float c6 = (float)(1.0 / 720.0), c7 = (float)(1.0 / 5040.0);
+  float y = __fmul_rn(t, kLog2e);
+  const bool flush = y < -125.0f;
+  if (flush) { t = 0.0f; y = 0.0f; }
+  const float n = floorf(__fadd_rn(y, 0.5f));
+  float x = __fsub_rn(t, __fmul_rn(n, kLn2Hi));
+  x = __fsub_rn(x, __fmul_rn(n, kLn2Lo));
+  float r = c7;
+  r = __fadd_rn(__fmul_rn(r, x), c6);
+  r = __fadd_rn(__fmul_rn(r, x), c5);
+  r = __fadd_rn(__fmul_rn(r, x), c4);
+  r = __fadd_rn(__fmul_rn(r, x), c3);
+  r = __fadd_rn(__fmul_rn(r, x), c2);
+  r = __fadd_rn(__fmul_rn(r, x), c1);
+  r = __fadd_rn(__fmul_rn(r, x), c0);
+  const float out = ldexpf(r, (int)n);
+  return flush ? 0.0f : out;
+}
+
+// ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011) -------------------
+__device__ __forceinline__ uint64_t philox_word(uint64_t c0, uint64_t c1, uint64_t k0, int word) {
+  const uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  const uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+  uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
+  uint64_t key0 = k0, key1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { key0 += kW0; key1 += kW1; }
+    const uint64_t hi0 = __umul64hi(kM0, x0), lo0 = kM0 * x0;
+    const uint64_t hi1 = __umul64hi(kM1, x2), lo1 = kM1 * x2;
+    const uint64_t n0 = hi1 ^ x1 ^ key0, n2 = hi0 ^ x3 ^ key1;
+    x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
+  }
+  return word == 0 ? x0 : word == 1 ? x1 : word == 2 ? x2 : x3;
+}
+
+// ---- radix select of the k-th largest order key of a row ------------------
+// Returns T (the k-th largest key) and `need`, the number of keys equal to T
+// that belong to the top k (those with the lowest indices).
+__device__ void radix_select(const float* zr, int n, int k, int* hist, uint32_t& T, int& need) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  need = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+    wave_lds_sync();
+    for (int j = lane; j < n; j += 64) {
+      const uint32_t key = order_key(zr[j]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    wave_lds_sync();
+    // lane L holds bins 255-4L .. 252-4L (descending digit order)
+    int c[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * lane - q]; s += c[q]; }
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int excl = incl - s;
+    int digit = 0, above = 0, run = excl;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (run < need && run + c[q] >= need) { digit = 255 - 4 * lane - q; above = run; }
+      run += c[q];
+    }
+    const uint64_t hit = __ballot(excl < need && incl >= need);
+    const int src = __ffsll((unsigned long long)hit) - 1;
+    digit = __shfl(digit, src, 64);
+    above = __shfl(above, src, 64);
+    need -= above;
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 255u << shift;
+    wave_lds_sync();
+  }
+  T = prefix;
+}
+
+__global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
+  __shared__ float zs[kZFloats];
+  __shared__ float qs[kMaxRows * 128];
+  __shared__ int hist_all[kMaskWaves * 256];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int R = a.rows_per_group;
+  const int ngroups = (a.nqb + R - 1) / R;
+  const int bh = blockIdx.x / ngroups;
+  const int i0 = (blockIdx.x % ngroups) * R;
+  const int nrows = min(R, a.nqb - i0);
+  const int n = a.nkb;
+  const int D = a.D;
+
+  // ---- A. logits --------------------------------------------------------
+  const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
+  for (int e = tid; e < nrows * D; e += kMaskThreads) qs[e] = qsrc[e];
+  __syncthreads();
+  for (int j = tid; j < n; j += kMaskThreads) {
+    float acc[kMaxRows];
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
+    const float* kr = a.kp + ((int64_t)bh * n + j) * D;
+    for (int d = 0; d < D; d += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
+#pragma unroll
+      for (int r = 0; r < kMaxRows; ++r) {
+        if (r < nrows) {
+          const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.x, kv.x));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
+        }
+      }
+    }
+    const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) {
+      if (r < nrows) {
+        float z = __fmul_rn(acc[r], a.scale);
+        if (a.log_cluster) z = __fadd_rn(z, lc);
+        if (z == 0.0f) z = 0.0f;                // -0 -> +0
+        zs[r * n + j] = z;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- B. per-row selection ------------------------------------------------
+  int* hist = hist_all + wave * 256;
+  const uint64_t below = lanes_below();
+  for (int r = wave; r < nrows; r += kMaskWaves) {
+    const int i = i0 + r;
+    const int64_t rowid = (int64_t)bh * a.nqb + i;
+    uint8_t* mrow = a.mask ? a.mask + rowid * n : nullptr;
+    int32_t* irow = a.idx + rowid * n;
+    float* wrow = a.logw ? a.logw + rowid * n : nullptr;
+    const bool dense = a.frame0_first >= 0 && i >= a.frame0_first && i <= a.frame0_last;
+    if (dense) {
+      for (int j = lane; j < n; j += 64) {
+        if (mrow) mrow[j] = 1;
+        irow[j] = j;
+        if (wrow) wrow[j] = 0.0f;
+      }
+      if (lane == 0) a.cnt[rowid] = n;
+      continue;
+    }
+    const float* zr = zs + r * n;
+
+    if (a.mode == 0) {
+      uint32_t T;
+      int need;
+      radix_select(zr, n, a.topk, hist, T, need);
+      int run_eq = 0, run_sel = 0;
+      for (int base = 0; base < n; base += 64) {
+        const int j = base + lane;
+        const bool in = j < n;
+        const uint32_t key = in ? order_key(zr[j]) : 0u;
+        const bool eq = in && key == T;
+        const uint64_t beq = __ballot(eq);
+        const int eq_rank = run_eq + __popcll(beq & below);
+        bool sel = in && (key > T || (eq && eq_rank < need));
+        if (in && j <= a.text_last) sel = true;
+        const uint64_t bsel = __ballot(sel);
+        const int pos = run_sel + __popcll(bsel & below);
+        if (in && mrow) mrow[j] = sel ? 1 : 0;
+        if (sel) {
+          irow[pos] = j;
+          if (wrow) wrow[pos] = 0.0f;
+        }
+        run_eq += __popcll(beq);
+        run_sel += __popcll(bsel);
+      }
+      if (lane == 0) a.cnt[rowid] = run_sel;
+      continue;
+    }
+
+    // ---- sampling ----------------------------------------------------------
+    // max and first argmax of z
+    float m = -INFINITY;
+    int am = n;
+    for (int j = lane; j < n; j += 64) {
+      const float z = zr[j];
+      if (z > m) { m = z; am = j; }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float om = __shfl_xor(m, s, 64);
+      const int oa = __shfl_xor(am, s, 64);
+      if (om > m || (om == m && oa < am)) { m = om; am = oa; }
+    }
+    // e_j, element j = lane + 64*mm
+    int P = 64;
+    while (P < n) P <<= 1;
+    const int per = P / 64;
+    float e[kMaxPerLane];
+#pragma unroll
+    for (int mm = 0; mm < kMaxPerLane; ++mm) {
+      const int j = lane + 64 * mm;
+      e[mm] = (mm < per && j < n) ? exp_le0(__fsub_rn(zr[j], m)) : 0.0f;
+    }
+    const float E = a.expected;
+    uint32_t cap = 0;
+    float c = 0.0f;
+    const bool all_in = (double)E >= (double)n;
+    if (!all_in) {
+      int ncap = 0;
+      for (int iter = 0; iter <= n + 1; ++iter) {
+        float v[kMaxPerLane];
+#pragma unroll
+        for (int mm = 0; mm < kMaxPerLane; ++mm) v[mm] = ((cap >> mm) & 1u) ? 0.0f : e[mm];
+        // halves-folding tree: in-lane levels, then across lanes
+#pragma unroll
+        for (int h = kMaxPerLane / 2; h >= 1; h >>= 1) {
+          if (h < per) {
+#pragma unroll
+            for (int mm = 0; mm < h; ++mm) v[mm] = __fadd_rn(v[mm], v[mm + h]);
+          }
+        }
+        float sig = v[0];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+          const float o = __shfl_down(sig, s, 64);
+          if (lane < s) sig = __fadd_rn(sig, o);
+        }
+        sig = __shfl(sig, 0, 64);
+        const float num = __fsub_rn(E, (float)ncap);
+        c = (num > 0.0f && sig > 0.0f) ? __fdiv_rn(num, sig) : 0.0f;
+        uint32_t grown = cap;
+#pragma unroll
+        for (int mm = 0; mm < kMaxPerLane; ++mm)
+          if (__fmul_rn(c, e[mm]) >= 1.0f) grown |= 1u << mm;
+        if (!__any(grown != cap)) break;
+        cap = grown;
+        ncap = wave_sum_int(__popc(cap));
+      }
+    }
+    // pi, draws
+    uint32_t selbits = 0;
+    float pi[kMaxPerLane];
+#pragma unroll
+    for (int mm = 0; mm < kMaxPerLane; ++mm) {
+      const int j = lane + 64 * mm;
+      pi[mm] = (all_in || ((cap >> mm) & 1u)) ? 1.0f : __fmul_rn(c, e[mm]);
+      if (mm < per && j < n) {
+        const uint64_t w = philox_word((uint64_t)rowid, (uint64_t)(j >> 2), a.seed, j & 3);
+        const float u = (float)(uint32_t)(w >> 40) * 5.9604644775390625e-08f;   // 2^-24
+        if (u < pi[mm]) selbits |= 1u << mm;
+      }
+    }
+    const bool any_sel = __any(selbits != 0);
+    if (!any_sel && (am & 63) == lane) {
+      // safeguard block: kept with weight 0
+#pragma unroll
+      for (int mm = 0; mm < kMaxPerLane; ++mm)
+        if (mm == (am >> 6)) { selbits |= 1u << mm; pi[mm] = 1.0f; }
+    }
+    int run_sel = 0;
+#pragma unroll
+    for (int mm = 0; mm < kMaxPerLane; ++mm) {
+      if (mm < per) {
+        const int j = lane + 64 * mm;
+        const bool in = j < n;
+        bool sel = in && ((selbits >> mm) & 1u);
+        float w = (sel && pi[mm] < 1.0f) ? -logf(pi[mm]) : 0.0f;
+        if (in && j <= a.text_last) { sel = true; w = 0.0f; }
+        const uint64_t bsel = __ballot(sel);
+        const int pos = run_sel + __popcll(bsel & below);
+        if (in && mrow) mrow[j] = sel ? 1 : 0;
+        if (sel) {
+          irow[pos] = j;
+          wrow[pos] = w;
+        }
+        run_sel += __popcll(bsel);
+      }
+    }
+    if (lane == 0) a.cnt[rowid] = run_sel;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mask(const MaskArgs& a, hipStream_t stream) {
+  const int ngroups = (a.nqb + a.rows_per_group - 1) / a.rows_per_group;
+  const int64_t grid = (int64_t)a.BH * ngroups;
+  hipLaunchKernelGGL(mask_kernel, dim3((unsigned)grid), dim3(kMaskThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,187 @@
+/*
+ * bsa.h -- C ABI of the block-sparse video attention library (libbsa.so,
+ * gfx950 / MI355X).
+ *
+ * The library computes, per attention head of a video diffusion transformer,
+ *
+ *   1. block summaries: the mean of the valid tokens of each query block and
+ *      each key block  (bsa_pool_blocks);
+ *   2. block scores, per-row selection and overrides: float32 block logits
+ *      z_ij = (q̄_i·k̄_j)/sqrt(D) (+ ln n_j), per-row top-k or importance
+ *      sampling, query blocks overlapping frame 0 forced dense, optional text
+ *      columns, and the compacted per-row block lists  (bsa_build_mask);
+ *   3. exact attention on the selected blocks only, with online softmax and
+ *      an optional additive per-block log-weight  (bsa_forward).
+ *
+ * Pages followed (title; section):
+ *   - "Attention matrix view: make only frame-0 query rows dense": sec. 1
+ *     token packing [text] + [frame0] + [frame1] + ...; sec. 2 frame-0 query
+ *     rows attend to every key/value token; sec. 4 block-level override
+ *     (first/last frame-0 query block formula); sec. 6 top-k mask built first,
+ *     frame-0 rows overwritten after; sec. 7 always keep text blocks.
+ *   - "Competition Domains Matter ... (EG-Sparse)": centroid-level softmax
+ *     weighted by cluster size (its Eq. 2); at-least-one-key-per-row safeguard.
+ *   - "AB-Attention: accurate block-sparse attention for video diffusion":
+ *     TL;DR and flowchart -- exact attention on selected key/value blocks;
+ *     blocks sampled in proportion to importance and reweighted by inverse
+ *     inclusion probability; key blocks smaller than a tile gathered into
+ *     full tiles.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are caller-owned device pointers (allocated by any HIP
+ *     allocator, e.g. PyTorch), contiguous, 16-byte aligned.  Q/K/V/O are
+ *     [B, H, seq_alloc, D] with D innermost.  The library never allocates,
+ *     frees or synchronizes; all work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and runs asynchronously.
+ *   - S = text_len + frames * latent_h * latent_w valid tokens;
+ *     nqb = ceil(S / q_block), nkb = ceil(S / k_block).  Rows >= S of an
+ *     input are never used as data (pad keys are excluded, pad query rows
+ *     produce 0), so they may hold anything, NaN included.
+ *   - Errors: every argument is validated on the host before any launch; a
+ *     non-OK status means nothing was enqueued, except BSA_ERR_HIP from a
+ *     failed launch.  bsa_last_error() gives a message (thread-local).  No
+ *     C++ exception crosses this boundary and no call exits the process.
+ *   - Entry points are reentrant; the only global state is the thread-local
+ *     error message.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, inconsistent geometry */
+  BSA_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels implement */
+  BSA_ERR_HIP = 3               /* a HIP runtime call failed; see bsa_last_error() */
+} bsa_status;
+
+typedef enum { BSA_DTYPE_BF16 = 0, BSA_DTYPE_F32 = 1 } bsa_dtype;
+
+typedef enum { BSA_SELECT_TOPK = 0, BSA_SELECT_SAMPLE = 1 } bsa_select_mode;
+
+/* Problem statement of the frame-0 page (sec. 4): text_len, latent_H x
+ * latent_W tokens per frame, q_block_size; plus batch, heads, head_dim, the
+ * key block size and the padded row count of every [B,H,seq_alloc,D] buffer.
+ * Supported: head_dim 64 or 128; q_block 32 or 64; k_block 16, 32 or 64;
+ * seq_alloc >= max(nqb*q_block, nkb*k_block). */
+typedef struct {
+  int32_t B, H;
+  int32_t text_len, frames, latent_h, latent_w;
+  int32_t head_dim;
+  int32_t q_block, k_block;
+  int32_t reserved;
+  int64_t seq_alloc;
+} bsa_geometry;
+
+/* Selection policy.
+ *   mode = BSA_SELECT_TOPK: each row keeps the k largest logits, larger
+ *     first, equal logits -> lower block index first; k = topk if topk > 0,
+ *     else ceil(keep_ratio * nkb) (in double) clamped to [1, nkb].
+ *   mode = BSA_SELECT_SAMPLE: Poisson sampling; block j is kept with
+ *     probability pi_j = min(1, c * e_j), e_j = exp(z_j - max z) (own float32
+ *     exp, Cody-Waite reduction + degree-7 Taylor), c water-filled so that
+ *     sum pi = fp32(keep_ratio * nkb); the uniform of block j of row
+ *     r = (b*H + h)*nqb + i is word j%4 of Philox4x64-10 at counter
+ *     (r, j/4, 0, 0), key (seed, 0), taken as (word >> 40) * 2^-24; kept iff
+ *     u < pi.  A kept block's log-weight is -ln pi_j (0 when pi_j = 1).  A
+ *     row with nothing drawn keeps its largest-logit block with weight 0.
+ *   frame0_dense: query blocks overlapping frame 0 keep every key block
+ *     (weight 0), applied after selection.
+ *   text_columns: every row also keeps the key blocks overlapping
+ *     [0, text_len) (weight 0), not counted against k.
+ *   log_cluster: add fp32(ln n_j) (n_j = valid tokens of key block j) to
+ *     the logits. */
+typedef struct {
+  int32_t mode;
+  int32_t topk;
+  double keep_ratio;
+  int32_t frame0_dense;
+  int32_t text_columns;
+  int32_t log_cluster;
+  int32_t reserved;
+  uint64_t seed;
+} bsa_mask_params;
+
+/* Derived sizes of a geometry (host only, no device work).  `p` may be NULL,
+ * then topk and expected are 0. */
+typedef struct {
+  int64_t S;
+  int32_t nqb, nkb;
+  int32_t frame0_first, frame0_last; /* -1, -1 if no frame */
+  int32_t text_last;                 /* last key block overlapping text, -1 if none */
+  int32_t topk;                      /* k of a top-k policy */
+  float expected;                    /* fp32(keep_ratio * nkb) of a sampling policy */
+  int32_t reserved;
+} bsa_derived;
+
+bsa_status bsa_derive(const bsa_geometry* g, const bsa_mask_params* p, bsa_derived* out);
+
+/* Block mean pooling (AB-Attention page, TL;DR "coarse summaries";
+ * EG-Sparse page, cluster centroids).
+ *   x:      [B, H, seq_alloc, D] of `dtype`.
+ *   block:  rows per block (the geometry's q_block for Q, k_block for K).
+ *   pooled: [B, H, ceil(S/block), D] float32, written.  For block i with
+ *           n = min(block, S - i*block) rows and channel d:
+ *           acc = 0; for t ascending: acc = fl32(acc + x[t][d]);
+ *           pooled = fl32(acc / n).  Bit-reproducible. */
+bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, int32_t block,
+                           float* pooled, void* stream);
+
+/* Block logits, selection, overrides and compaction (frame-0 page secs. 4,
+ * 6, 7; EG-Sparse page Eq. 2 and the one-key safeguard; AB-Attention page
+ * sampling and reweighting).
+ *   q_pooled: [B, H, nqb, D] float32 (bsa_pool_blocks with q_block).
+ *   k_pooled: [B, H, nkb, D] float32 (bsa_pool_blocks with k_block).
+ *   logits: z = fl32(fl32(sum_d in ascending d of fl32(q̄_d * k̄_d)) *
+ *           fp32(1/sqrt(D))) (+ fp32(ln n_j), one more rounding), -0 -> +0.
+ *   mask:   [B, H, nqb, nkb] uint8 (1 = block selected) or NULL.
+ *   kv_cnt: [B, H, nqb] int32, number of selected blocks per row (>= 1).
+ *   kv_idx: [B, H, nqb, nkb] int32, row stride nkb; the first kv_cnt
+ *           entries of a row are its selected block indices, ascending; the
+ *           rest are left unwritten.
+ *   log_w:  [B, H, nqb, nkb] float32 or NULL (required for SAMPLE): the
+ *           log-weight of list slot p of each row, 0 for top-k rows.
+ *   nkb is limited to 8192 for top-k and 2048 for sampling
+ *   (BSA_ERR_UNSUPPORTED beyond). */
+bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bsa_geometry* g,
+                          const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
+                          int32_t* kv_idx, float* log_w, void* stream);
+
+/* Exact attention on the selected blocks (AB-Attention page, TL;DR and
+ * "Gather kernel"/"Reweighted attention" flowchart nodes; frame-0 page sec. 2).
+ *   q, k, v: [B, H, seq_alloc, D] of `dtype` (bf16 or f32; f32 is rounded
+ *            to bf16 for the matrix products).
+ *   kv_cnt, kv_idx: row lists as written by bsa_build_mask (row stride nkb).
+ *            Indices outside [0, nkb) are skipped.
+ *   log_w:   NULL or [B, H, nqb, nkb] float32 per-slot log-weights.
+ *   softmax_scale: 0 -> fp32(1/sqrt(D)).
+ *   For query token t of block i: o_t = sum_u softmax_u(q_t·k_u * scale +
+ *   log_w[i][p(u)]) v_u over the tokens u < S of the listed key blocks
+ *   (p(u) = list slot of u's block); key blocks smaller than 64 tokens are
+ *   gathered four/two per 64-key tile.  bf16 matrix products, float32
+ *   accumulation and softmax.
+ *   out:     [B, H, seq_alloc, D] of `dtype`; rows >= S and rows with an
+ *            empty list are written as 0.
+ *   lse:     NULL or [B, H, seq_alloc] float32, ln sum_u exp(logit_u);
+ *            -inf for rows >= S and empty rows. */
+bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtype,
+                       const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                       const float* log_w, float softmax_scale, void* out, float* lse,
+                       void* stream);
+
+const char* bsa_status_string(int32_t status);
+const char* bsa_last_error(void);
+int32_t bsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -28,8 +28,7 @@ def inputs_of(w: W.Workload, heads=None, pad_value=0.0):
 def tiny(text_len=5, frames=2, lh=3, lw=5, bq=8, bk=8, D=16, H=2, B=1, **kw):
     """A small ragged workload (S not a multiple of the block sizes)."""
     base = W.workload("tiny_f32")
-    S = text_len + frames * lh * lw
-    align = max(bq, bk)
+    align = kw.pop("align", max(bq, bk))
     M = kw.pop("centroids", 4)
     grid = kw.pop("grid", (2, 2) if M == 4 else (1, M))
     return base.replace(name="tiny_ragged", B=B, H=H, D=D, text_len=text_len, frames=frames,

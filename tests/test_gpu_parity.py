@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: pooled means, block masks, counts and per-row lists (and the
+sampling log-weights to 2 ulp, since ln is the GPU's own).  Attention output
+within max-abs 2e-2 / mean-abs 2e-3 (bf16 in, float32 accumulate).  Small
+workloads are compared on every row; the full-size workloads (launched
+exactly as bench.py launches them) on sampled rows the oracle computes one by
+one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import geometry_of, inputs_of, params_of, tiny
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+bsa = pytest.importorskip("block_sparse_attention_42_amd")
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _geo(w):
+    return bsa.Geometry(w.B, w.H, w.text_len, w.frames, w.latent_h, w.latent_w, w.D,
+                        w.q_block, w.k_block, w.seq_alloc)
+
+
+def _mp(w):
+    return bsa.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio,
+                          frame0_dense=w.frame0_dense, text_columns=w.text_columns,
+                          log_cluster=w.log_cluster, seed=w.sample_seed)
+
+
+def _dev(w, a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if w.dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def run_gpu(w, q, k, v, want_lse=True):
+    """The whole path on the GPU, through the C ABI."""
+    _say(f"[gpu] {w.name} B={w.B} H={w.H} S={w.S} D={w.D} bq={w.q_block} bk={w.k_block} mode={w.mode}")
+    g = _geo(w)
+    qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
+    qp = bsa.bsa_pool_blocks(qd, g, g.q_block)
+    kp = bsa.bsa_pool_blocks(kd, g, g.k_block)
+    mask, cnt, idx, logw = bsa.bsa_build_mask(qp, kp, g, _mp(w))
+    out, lse = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, want_lse=want_lse)
+    torch.cuda.synchronize()
+    r = dict(qp=qp.cpu().numpy(), kp=kp.cpu().numpy(), mask=mask.cpu().numpy().astype(bool),
+             cnt=cnt.cpu().numpy(), idx=idx.cpu().numpy(),
+             logw=None if logw is None else logw.cpu().numpy(),
+             out=out.float().cpu().numpy(), lse=None if lse is None else lse.cpu().numpy())
+    return r
+
+
+def _check_lists(w, r, om, ocnt, oidx, ologw, rows):
+    for (b, h, i) in rows:
+        assert np.array_equal(r["mask"][b, h, i], om[b, h, i]), (w.name, b, h, i)
+        c = ocnt[b, h, i]
+        assert r["cnt"][b, h, i] == c, (w.name, b, h, i)
+        assert np.array_equal(r["idx"][b, h, i, :c], oidx[b, h, i, :c]), (w.name, b, h, i)
+        if w.mode == "sample":
+            gw = r["logw"][b, h, i, :c].astype(np.float64)
+            ow = ologw[b, h, i, :c].astype(np.float64)
+            assert np.all(np.abs(gw - ow) <= 2.5e-7 * np.maximum(1.0, np.abs(ow))), (w.name, b, h, i)
+
+
+def _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qblocks_by_head):
+    errs = []
+    for (b, h), qbl in qblocks_by_head.items():
+        o, l = oracle.attention_head(q[b, h], k[b, h], v[b, h], g, ocnt[b, h], oidx[b, h], ologw[b, h],
+                                     q_blocks=qbl)
+        rows = np.concatenate([np.arange(i * g.q_block, min((i + 1) * g.q_block, g.seq_alloc)) for i in qbl])
+        got = r["out"][b, h, rows].astype(np.float64)
+        assert np.isfinite(got).all()
+        err = np.abs(got - o)
+        errs.append(err)
+        assert err.max() <= MAX_ABS, (w.name, b, h, err.max())
+        valid = rows < g.S
+        gl = r["lse"][b, h, rows]
+        assert np.all(np.isneginf(gl[~valid]))
+        tol = 2e-3 if w.dtype == "bf16" else 5e-2     # float32 inputs are rounded to bf16 on the GPU
+        assert np.allclose(gl[valid], l[valid], atol=tol, rtol=1e-4), (w.name, b, h)
+        assert np.all(got[~valid] == 0)
+    allerr = np.concatenate([e.ravel() for e in errs])
+    _say(f"    out max|err| {allerr.max():.3e} mean|err| {allerr.mean():.3e} over {allerr.size} values")
+    assert allerr.mean() <= MEAN_ABS
+
+
+SMALL = {
+    "tiny_f32": W.workload("tiny_f32"),
+    "small_bf16": W.workload("small_bf16"),
+    "ragged_bf16_k16_sample": tiny(text_len=37, frames=5, lh=9, lw=13, bq=64, bk=16, D=128, H=3,
+                                  dtype="bf16", mode="sample", topk=0, keep_ratio=0.15, sample_seed=7,
+                                  centroids=8, grid=(2, 4), align=64),
+    "ragged_bf16_k32_text_lc": tiny(text_len=70, frames=4, lh=11, lw=15, bq=64, bk=32, D=128, H=2,
+                                   dtype="bf16", mode="topk", topk=0, keep_ratio=0.2, text_columns=True,
+                                   log_cluster=True, centroids=8, grid=(2, 4), align=64),
+    "ragged_f32_d64_q32_k16": tiny(text_len=19, frames=3, lh=7, lw=9, bq=32, bk=16, D=64, H=2,
+                                  dtype="f32", mode="topk", topk=5, text_columns=True, centroids=4,
+                                  grid=(2, 2), align=32),
+    "ragged_bf16_d64_sample_k64": tiny(text_len=0, frames=6, lh=10, lw=13, bq=64, bk=64, D=64, H=2,
+                                      dtype="bf16", mode="sample", topk=0, keep_ratio=0.3, sample_seed=99,
+                                      frame0_dense=False, centroids=8, grid=(2, 4), align=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workloads_every_row(name):
+    w = SMALL[name]
+    g = geometry_of(w)
+    q, k, v = inputs_of(w, pad_value=np.nan)
+    r = run_gpu(w, q, k, v)
+    oqp = oracle.pool_blocks(q, g.S, g.q_block)
+    okp = oracle.pool_blocks(k, g.S, g.k_block)
+    assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w))
+    rows = [(b, h, i) for b in range(g.B) for h in range(g.H) for i in range(g.nqb)]
+    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    heads = [(b, h) for b in range(g.B) for h in range(g.H)]
+    if g.S > 4096:   # every row of two heads, sampled rows of the others
+        rng = np.random.default_rng(0)
+        qbl = {bh: (list(range(g.nqb)) if n < 2 else sorted(set(rng.integers(0, g.nqb, 6).tolist()) | {0, g.nqb - 1}))
+               for n, bh in enumerate(heads)}
+    else:
+        qbl = {bh: list(range(g.nqb)) for bh in heads}
+    _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qbl)
+
+
+FULL = ["wan_1p3b_keep10", "wan_1p3b_sampled_k16", "hunyuan_keep08"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    w = W.workload(name)
+    g = geometry_of(w)
+    q, k, v = inputs_of(w)
+    r = run_gpu(w, q, k, v)
+    oqp = oracle.pool_blocks(q, g.S, g.q_block)
+    okp = oracle.pool_blocks(k, g.S, g.k_block)
+    assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
+    rng = np.random.default_rng(1)
+    f0 = list(g.frame0_q_blocks())
+    rows = []
+    for h in sorted(set([0, g.H - 1] + rng.integers(0, g.H, 2).tolist())):
+        picks = {f0[0], f0[-1], f0[-1] + 1, g.nqb - 1, g.nqb // 2} | set(rng.integers(0, g.nqb, 6).tolist())
+        rows += [(0, h, i) for i in sorted(picks)]
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w), rows=rows)
+    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    # every row non-empty, every list ascending (a property that holds at any size)
+    assert (r["cnt"] >= 1).all()
+    if w.mode == "topk":
+        k_ = oracle.topk_count(g.nkb, w.topk, w.keep_ratio)
+        sparse = np.ones(g.nqb, bool)
+        sparse[f0] = False
+        extra = len(g.text_k_blocks()) if w.text_columns else 0
+        assert np.all(r["cnt"][:, :, sparse] >= k_) and np.all(r["cnt"][:, :, sparse] <= k_ + extra)
+        assert np.all(r["cnt"][:, :, f0] == g.nkb)
+    qbl = {}
+    for (b, h, i) in rows[::2]:
+        qbl.setdefault((b, h), []).append(i)
+    _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qbl)
+
+
+def test_forward_arbitrary_lists_weights_and_nan_pads():
+    w = tiny(text_len=21, frames=4, lh=9, lw=11, bq=64, bk=16, D=128, H=3, dtype="bf16", align=64,
+             centroids=4, grid=(2, 2))
+    g = geometry_of(w)
+    q, k, v = inputs_of(w, pad_value=np.nan)
+    rng = np.random.default_rng(5)
+    cnt = np.zeros((g.B, g.H, g.nqb), np.int32)
+    idx = np.full((g.B, g.H, g.nqb, g.nkb), -1, np.int32)
+    lw = np.zeros((g.B, g.H, g.nqb, g.nkb), np.float32)
+    for h in range(g.H):
+        for i in range(g.nqb):
+            c = int(rng.integers(0, g.nkb + 1)) if (h, i) != (1, 2) else 0    # one empty row
+            js = np.sort(rng.choice(g.nkb, c, replace=False))
+            cnt[0, h, i] = c
+            idx[0, h, i, :c] = js
+            lw[0, h, i, :c] = rng.normal(0, 1.5, c).astype(np.float32)
+    gg = _geo(w)
+    qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
+    out, lse = bsa.bsa_forward(qd, kd, vd, gg, torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(lw).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    r = dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+    _check_out(w, r, q, k, v, g, cnt, idx, lw, {(0, h): list(range(g.nqb)) for h in range(g.H)})
+    assert np.all(r["out"][0, 1, 2 * 64:3 * 64] == 0) and np.all(np.isneginf(r["lse"][0, 1, 2 * 64:3 * 64]))
+    # an explicit softmax scale
+    out2, _ = bsa.bsa_forward(qd, kd, vd, gg, torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda(),
+                              torch.from_numpy(lw).cuda(), softmax_scale=0.05)
+    torch.cuda.synchronize()
+    o, _ = oracle.attention_head(q[0, 0], k[0, 0], v[0, 0], g, cnt[0, 0], idx[0, 0], lw[0, 0], softmax_scale=0.05)
+    assert np.abs(out2.float().cpu().numpy()[0, 0, :o.shape[0]] - o).max() <= MAX_ABS
+
+
+def test_deterministic_reruns():
+    w = SMALL["ragged_bf16_k16_sample"]
+    q, k, v = inputs_of(w)
+    a = run_gpu(w, q, k, v)
+    b = run_gpu(w, q, k, v)
+    for key in ("qp", "kp", "mask", "cnt", "out", "lse", "logw"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
