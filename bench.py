@@ -33,7 +33,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan_1p3b_keep10")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-qblocks", type=int, default=48)
+    ap.add_argument("--cpu-sample-qblocks", type=int, default=1024)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -88,6 +90,16 @@ def cpu_baseline(w, q, k, v, nblocks):
 
 def main():
     a = _args()
+    if a.calibrate_copy_mib:
+        import torch
+        n = a.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU: the path has no multi-GPU part in this build "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)

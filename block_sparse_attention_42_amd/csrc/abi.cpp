@@ -228,6 +228,9 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
     return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
   if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
     return fail(BSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (d.nkb > 8192) return fail(BSA_ERR_UNSUPPORTED, "nkb %d > 8192", d.nkb);
+  if (g->seq_alloc * g->head_dim * (dtype == BSA_DTYPE_F32 ? 4 : 2) >= (1LL << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "one head of q/k/v exceeds 2 GiB");
   const int64_t units = (int64_t)g->B * g->H * d.nqb;
   if (units > 0x7fffffffLL) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
   bsa::FwdArgs a;

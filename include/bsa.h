@@ -170,7 +170,9 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
  *   out:     [B, H, seq_alloc, D] of `dtype`; rows >= S and rows with an
  *            empty list are written as 0.
  *   lse:     NULL or [B, H, seq_alloc] float32, ln sum_u exp(logit_u);
- *            -inf for rows >= S and empty rows. */
+ *            -inf for rows >= S and empty rows.
+ *   Limits: nkb <= 8192 and one head of q/k/v below 2 GiB
+ *   (BSA_ERR_UNSUPPORTED beyond). */
 bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtype,
                        const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
                        const float* log_w, float softmax_scale, void* out, float* lse,
