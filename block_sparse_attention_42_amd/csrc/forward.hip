@@ -31,8 +31,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFwdThreads = 128;   // two waves: each owns half of the query block's rows
-constexpr int kWaves = 2;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kListCap = 2048;     // list entries of a row cached in LDS (the rest read from global)
 
@@ -46,9 +44,11 @@ struct Ld8<bf16_t> {
   }
 };
 
+// Two floats as two bf16 (round to nearest even) in one dword: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
 }
 
 template <>
@@ -122,54 +122,65 @@ __device__ __forceinline__ void store8<float>(float* dst, const float (&v)[8]) {
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// LDS chunk swizzles (16-byte chunks of a row of D bf16).  K rows are read
-// as 16-byte A-operand pieces by 16 lanes at once; V rows are read with the
-// transposing 8-byte load by groups of 4 lanes per row.  The XOR patterns
-// below put those simultaneous accesses on distinct banks.
+
+// x combined with the same register of lane ^ 32 (one v_permlane32_swap).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS chunk swizzles of the 32-row K and V sub-tiles (16-byte chunks of a row
+// of D bf16).  K rows are read as 16-byte A-operand pieces, 16 consecutive
+// rows at the same logical chunk per access; V rows are read with the
+// transposing 8-byte load, 4 consecutive rows x 4 chunks per 16 lanes.  The
+// XOR patterns put each access group on distinct banks; they only touch chunk
+// bits, so every address is (lane base) ^ (per-fragment constant).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (D == 128) return 4 * (r >> 3) + (r & 3);                 // 0..15
-  else return ((r >> 1) & 1) | (((r >> 3) & 3) << 1);                    // 0..7
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
 }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) {                            // even: keeps chunk pairs
-  if constexpr (D == 128) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));  // 0..14
-  else return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));              // 0..6
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (D == 128) return 4 * (r & 3);
+  else return 4 * ((r >> 1) & 1);
 }
 
-// Row of the 32-key sub-tile supplied by A-operand row m of S^T M-tile mt.
-// With this order the accumulator rows a lane holds for M-tiles 0 and 1 are
-// the 8 consecutive keys 8*(lane/16) + 0..7 -- exactly the K-range the lane
-// supplies as B operand of O^T += V^T P^T.
-__device__ __forceinline__ int a_row(int mt, int m) { return 8 * (m >> 2) + 4 * mt + (m & 3); }
-
 template <typename T, int D, int QROWS, int BK>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int RW = QROWS / kWaves;   // query rows per wave
-  constexpr int NT = RW / 16;          // query column tiles of S^T / O^T
-  constexpr int DC = D / 32;           // K-chunks of the Q.K contraction
-  constexpr int DT = D / 16;           // d row tiles of O^T
+__global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
+  constexpr bool kDma = sizeof(T) == 2;  // bf16 tiles go HBM -> LDS directly; f32 is converted in registers
+  constexpr int NW = QROWS / 32;       // waves: each owns 32 query rows
+  constexpr int NTH = NW * 64;         // threads
+  constexpr int KC = D / 16;           // K-chunks of the Q.K contraction (32x32x16)
+  constexpr int DT = D / 32;           // d tiles of O^T
   constexpr int KCH = D / 8;           // 16-byte chunks per row
   constexpr int SUB = 32;              // keys per sub-tile
   constexpr int TILE_E = SUB * D;      // bf16 elements of one K (or V) sub-tile
-  constexpr int NLD = SUB * KCH / kFwdThreads;   // 16-byte loads per thread per operand
-  constexpr int RPL = kFwdThreads / KCH;         // tile rows covered by one load round
-  constexpr int NBLK = BK >= SUB ? 1 : SUB / BK; // key blocks per sub-tile
+  constexpr int NLD = SUB * KCH / NTH; // 16-byte loads per thread per operand
+  constexpr int RPL = NTH / KCH;       // tile rows covered by one load round
+  constexpr int NBLK = BK >= SUB ? 1 : SUB / BK;   // key blocks per sub-tile
+  constexpr int PART = SUB / NBLK;
   constexpr int OS = D + 4;            // LDS row stride of the output staging (floats)
   constexpr float kTau = 8.0f;         // lazy rescale: tolerated growth of the running max (log2)
-  static_assert(NT >= 1 && NLD >= 1 && NBLK <= 2, "tile shape");
-  constexpr int kTileHalves = 2 * 2 * TILE_E;                     // bf16 units
-  constexpr int kStageHalves = QROWS * OS * 2;                     // output staging, bf16 units
-  // two stages of (K, V) sub-tiles; reused for the output rows at the end
+  static_assert(NW >= 1 && NLD >= 1 && NBLK <= 2, "tile shape");
+  constexpr int kTileHalves = 4 * TILE_E;          // K0, V0, K1, V1 (bf16 units)
+  constexpr int kStageHalves = QROWS * OS * 2;     // output staging (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kTileHalves > kStageHalves ? kTileHalves : kStageHalves];
   __shared__ uint16_t lst[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;           // query column (S^T, O^T) / A-operand row
-  const int grp = lane >> 4;           // 0..3: K sub-range of the operands
+  const int qc = lane & 31;            // query column of S^T / O^T, A-operand row
+  const int hf = lane >> 5;            // 0/1: K half of the operands, row half of the accumulators
 
   // heaviest-first order: all heads of query block 0, then of block 1, ...
   const int bh = blockIdx.x % a.BH;
@@ -183,11 +194,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const T* Qb = reinterpret_cast<const T*>(a.q) + (int64_t)bh * a.seq_alloc * D;
   const T* Kb = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.seq_alloc * D;
   const T* Vb = reinterpret_cast<const T*>(a.v) + (int64_t)bh * a.seq_alloc * D;
-  const int64_t q0 = (int64_t)qb * a.q_block + wave * RW;     // this wave's first row
+  const int64_t q0 = (int64_t)qb * a.q_block + wave * 32;     // this wave's first row
   const int S32 = (int)a.S;
 
   // ---- the row's block list in LDS (entries past kListCap read from global) ----
-  for (int e = tid; e < min(cnt, kListCap); e += kFwdThreads) {
+  for (int e = tid; e < min(cnt, kListCap); e += NTH) {
     const int j = list[e];
     lst[e] = (j >= 0 && j < a.nkb) ? (uint16_t)j : (uint16_t)0xffff;
   }
@@ -205,31 +216,33 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     }
     return __builtin_amdgcn_readfirstlane(j);     // wave-uniform
   };
+  // log2-domain weight of list slot pos (uniform load; only in weighted calls)
+  auto bias_at = [&](int pos) -> float {
+    if (!lw) return 0.0f;
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(lw[pos]))) * 1.4426950408889634f;
+  };
 
   const uint32_t nbytes = (uint32_t)a.seq_alloc * (uint32_t)D * (uint32_t)sizeof(T);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, (int)nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, (int)nbytes, 0x00020000);
 
-  // ---- Q^T fragments (B operand of S^T = K Q^T), kept for the whole row ----
-  bf16x8 qf[NT][DC];
+  // ---- Q^T fragments (B operand of S^T = K Q^T): Q[q][16c + 8hf .. +7] ----
+  bf16x8 qf[KC];
+  {
+    const int64_t row = q0 + qc;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int64_t row = q0 + nt * 16 + col;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
+    for (int c = 0; c < KC; ++c) {
       uint4 r = make_uint4(0, 0, 0, 0);
-      if (row < a.S) r = Ld8<T>::raw(Qb + row * D + dc * 32 + grp * 8);
-      qf[nt][dc] = as_frag(r);
+      if (row < a.S) r = Ld8<T>::raw(Qb + row * D + c * 16 + hf * 8);
+      qf[c] = as_frag(r);
     }
   }
 
   // ---- per-thread constant offsets ----
-  // Staging load n of this thread fills LDS chunk n*128 + tid: tile row
-  // srow(n) = n*RPL + tid/KCH, holding logical chunk (tid % KCH) ^ swizzle(row).
-  // Its global element offset is key0(part) * D + (row - part*PART) * D + chunk*8;
-  // the part of load n is the same for every thread, so only the last two terms
-  // (kc/vc) are per-thread constants.
-  constexpr int PART = SUB / NBLK;
+  // Tile load n of this thread fills LDS chunk n*NTH + tid: tile row
+  // r = n*RPL + tid/KCH, holding logical chunk (tid % KCH) ^ swizzle(r).  Its
+  // global element offset is key0(part) * D + (r - part*PART) * D + chunk*8,
+  // and the part of load n is the same for every thread.
   int rin[NLD];
   uint32_t kc[NLD], vc[NLD];
 #pragma unroll
@@ -239,213 +252,199 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     kc[n] = (uint32_t)(rin[n] * D + ((tid % KCH) ^ swz_k<D>(r)) * 8);
     vc[n] = (uint32_t)(rin[n] * D + ((tid % KCH) ^ swz_v<D>(r)) * 8);
   }
-  // K A-operand reads.  For row r = a_row(mt, col) the swizzled chunk is
-  // (4*dc + grp) ^ swz_k(r) = (4*dc) ^ (grp ^ swz_k(r)), and the row term has
-  // zero bits where the chunk index lives, so byte address = ka ^ (dc * 64),
-  // plus 4 rows (8*D bytes) for mt = 1 (row + 4 leaves swz_k unchanged).
-  const uint32_t ka = [&] {
-    const int r = a_row(0, col);
-    return (uint32_t)(r * KCH * 16) | (uint32_t)(((uint32_t)grp ^ (uint32_t)swz_k<D>(r)) * 16);
-  }();
-  // V^T transposing reads for (dt, hh): row r = 8*grp + 4*hh + col/4, logical
-  // chunk 2*dt + (col&3)/2, pair swizzle s: byte address = va ^ (dt * 32), plus
-  // 4 rows (8*D bytes) for hh = 1 (row + 4 leaves swz_v unchanged).
+  // K A-operand read of chunk c: tile row qc, logical chunk 2c + hf:
+  // byte address ka ^ (c * 32).
+  const uint32_t ka = (uint32_t)(qc * KCH * 16) | (uint32_t)((hf ^ swz_k<D>(qc)) * 16);
+  // V^T A-operand transposing reads: 16-lane group g = lane/16 covers d columns
+  // 16*(g & 1) + [0, 16) of d tile dt; lane i of the group addresses tile row
+  // 16c + 8hh + 4hf + i/4 and columns 32dt + 16(g & 1) + 4(i & 3):
+  // byte address va ^ (dt * 64) + (16c + 8hh) rows.
   const uint32_t va = [&] {
-    const int r = 8 * grp + (col >> 2);
-    return (uint32_t)(r * D * 2) | (uint32_t)(swz_v<D>(r) * 16) | (uint32_t)(((col & 3) >> 1) * 16) |
-           (uint32_t)((col & 1) * 8);
+    const int i = lane & 15, g = lane >> 4;
+    const int r = 4 * hf + (i >> 2);
+    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
+    return (uint32_t)(r * D * 2) | (uint32_t)((lc ^ swz_v<D>(r)) * 16) | (uint32_t)((i & 1) * 8);
   }();
 
-  float m_run[NT];
-  f32x4 o[DT][NT], lacc[NT];           // O^T and the row sums (ones-row MFMA)
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 o[DT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const bf16x8 ones = as_frag(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-  // ---- sub-tile geometry: key blocks, first key, valid keys, log2 weight ----
+  // ---- sub-tile geometry: first key, valid keys and log2 weight of each part ----
   struct SubInfo {
-    int key0[NBLK];      // first key of each block part, or -1
-    int valid[NBLK];     // valid keys of each part (0..min(BK,32))
+    int key0[NBLK];      // first key of each part (0 if none)
+    int valid[NBLK];     // valid keys of each part
     float bias[NBLK];
   };
   auto info = [&](int u) {
     SubInfo si;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
-      const int g = u * SUB + b * (SUB / NBLK);
+      const int g = u * SUB + b * PART;
       const int pos = g / BK;
       const int j = block_at(pos);
       const int key0 = j * BK + g % BK;
-      si.key0[b] = j >= 0 ? key0 : -1;
-      si.valid[b] = j >= 0 ? min(max(S32 - key0, 0), SUB / NBLK) : 0;
-      si.bias[b] = (lw && j >= 0) ? lw[pos] * 1.4426950408889634f : 0.0f;
+      si.key0[b] = j >= 0 ? key0 : 0;
+      si.valid[b] = j >= 0 ? min(max(S32 - key0, 0), PART) : 0;
+      si.bias[b] = j >= 0 ? bias_at(pos) : 0.0f;
     }
     return si;
   };
 
-  // ---- staging: both waves load half of a sub-tile, 16 bytes per load ----
-  uint4 kst[NLD], vst[NLD];
-  auto stage = [&](int u) {
-    const SubInfo si = info(u);
+  auto kbuf = [&](int b) { return tiles + b * 2 * TILE_E; };
+  auto vbuf = [&](int b) { return tiles + b * 2 * TILE_E + TILE_E; };
+
+  // ---- a sub-tile's K and V rows -> LDS buffer b ----
+  uint4 kst[kDma ? 1 : NLD], vst[kDma ? 1 : NLD];   // f32 only: staged in registers
+  auto load_tiles = [&](const SubInfo& si, int b) {
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-      const int b = (n * RPL) / PART;                // the part is the same for all threads of load n
-      const bool ok = rin[n] < si.valid[b];
-      const uint32_t base = (uint32_t)si.key0[b] * (uint32_t)D;
-      kst[n] = BufLd8<T>::load(rk, ok ? base + kc[n] : kOob);
-      vst[n] = BufLd8<T>::load(rv, ok ? base + vc[n] : kOob);
+      const int part = (n * RPL) / PART;
+      const bool ok = rin[n] < si.valid[part];
+      const uint32_t base = (uint32_t)si.key0[part] * (uint32_t)D;
+      if constexpr (kDma) {
+        // this wave's 64 lanes fill 1 KB of LDS at chunk n*NTH + 64*wave
+        const uint32_t kb = ok ? (base + kc[n]) * 2u : kOob;
+        const uint32_t vb = ok ? (base + vc[n]) * 2u : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)kb, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)vb, 0, 0, 0);
+      } else {
+        kst[n] = BufLd8<T>::load(rk, ok ? base + kc[n] : kOob);
+        vst[n] = BufLd8<T>::load(rv, ok ? base + vc[n] : kOob);
+      }
     }
-  };
-  auto commit = [&](int stage_buf) {
-    uint16_t* tk = tiles + stage_buf * 2 * TILE_E;
-    uint16_t* tv = tk + TILE_E;
+    if constexpr (!kDma) {
 #pragma unroll
-    for (int n = 0; n < NLD; ++n) {
-      *reinterpret_cast<uint4*>(tk + (n * kFwdThreads + tid) * 8) = kst[n];
-      *reinterpret_cast<uint4*>(tv + (n * kFwdThreads + tid) * 8) = vst[n];
+      for (int n = 0; n < NLD; ++n) {
+        *reinterpret_cast<uint4*>(kbuf(b) + (n * NTH + tid) * 8) = kst[n];
+        *reinterpret_cast<uint4*>(vbuf(b) + (n * NTH + tid) * 8) = vst[n];
+      }
     }
   };
 
-  // ---- one sub-tile of attention from LDS buffer `buf` ----
-  auto compute = [&](int u, const int buf) {
-    const unsigned char* tk = reinterpret_cast<const unsigned char*>(tiles) + buf * 2 * TILE_E * 2;
-    const unsigned char* tv = tk + TILE_E * 2;
-    const SubInfo si = info(u);
-    // this lane's 8 accumulator rows are tile rows 8*grp .. 8*grp+7 (one part)
-    const int part = NBLK == 1 ? 0 : (grp >> 1);
-    const int lim = min(max(si.valid[NBLK == 1 ? 0 : part] - (NBLK == 1 ? 8 * grp : 8 * (grp & 1)), 0), 8);
-    float bias = si.bias[0];
-    if constexpr (NBLK == 2) bias = part ? si.bias[1] : si.bias[0];
+  // ---- one sub-tile: S^T = K Q^T, online softmax, O^T += V^T P^T ----
+  // accumulator register r of this lane is tile row 8*(r/4) + 4*hf + r%4
+  auto compute = [&](const SubInfo& si, int b) {
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbuf(b));
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf(b));
+    f32x16 sc = f32x16{};
+    {
+      bf16x8 kf[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kf[c] = as_frag(*reinterpret_cast<const uint4*>(kt + (ka ^ (uint32_t)(c * 32))));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], sc, 0, 0, 0);
+    }
     bool full = true;
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) full = full && si.valid[b] == SUB / NBLK;
-
-    // S^T = K Q^T
-    f32x4 sacc[2][NT];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      bf16x8 kf[DC];
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        kf[dc] = as_frag(*reinterpret_cast<const uint4*>(tk + mt * (8 * D) + (ka ^ (uint32_t)(dc * 64))));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[dc], qf[nt][dc], c, 0, 0, 0);
-        sacc[mt][nt] = c;
-      }
-    }
+    for (int p = 0; p < NBLK; ++p) full = full && si.valid[p] == PART;
     if (!full) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            if (4 * mt + r >= lim) sacc[mt][nt][r] = -INFINITY;
-    }
-    // row max of the raw scores (scale > 0; the lane's 8 keys share one weight)
-    bool grow = false;
-    float mrow[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][nt][0], sacc[0][nt][1]), fmaxf(sacc[0][nt][2], sacc[0][nt][3])),
-                       fmaxf(fmaxf(sacc[1][nt][0], sacc[1][nt][1]), fmaxf(sacc[1][nt][2], sacc[1][nt][3])));
-      mx = mx * a.scale_log2 + bias;
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mrow[nt] = mx;
-      grow |= mx > m_run[nt] + kTau;
-    }
-    // lazy rescale: the reference max only moves when a row's max grows by more
-    // than kTau (so p <= 2^kTau); O and l are rescaled only then
-    if (__any(grow)) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float m_new = mrow[nt] > m_run[nt] + kTau ? mrow[nt] : m_run[nt];
-        const float alpha = fast_exp2(m_run[nt] - (m_new == -INFINITY ? 0.0f : m_new));
-        m_run[nt] = m_new;
-        lacc[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int p = row / PART;
+        if (row - p * PART >= si.valid[p]) sc[r] = -INFINITY;
       }
     }
-    // p = exp2(s * scale + bias - m); P^T as B operand (keys 8*grp + e)
-    bf16x8 pb[NT];
+    // row max: the lane's 16 keys, then lane ^ 32 (scale > 0, one weight per part)
+    const float mx0 = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    const float mx1 = fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])), fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15])));
+    float mx;
+    if constexpr (NBLK == 2) mx = fmaxf(mx0 * a.scale_log2 + si.bias[0], mx1 * a.scale_log2 + si.bias[1]);
+    else mx = fmaxf(mx0, mx1) * a.scale_log2 + si.bias[0];
+    mx = max_xor32(mx);
+    // lazy rescale: the reference max moves only when the row max grows by more
+    // than kTau (so p <= 2^kTau); O and l are rescaled only then
+    if (__any(mx > m_run + kTau)) {
+      const float m_new = mx > m_run + kTau ? mx : m_run;
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float off = bias - (m_run[nt] == -INFINITY ? 0.0f : m_run[nt]);
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(sacc[e >> 2][nt][e & 3] * a.scale_log2 + off);
-      uint4 w;
-      w.x = pack_bf16x2(p[0], p[1]);
-      w.y = pack_bf16x2(p[2], p[3]);
-      w.z = pack_bf16x2(p[4], p[5]);
-      w.w = pack_bf16x2(p[6], p[7]);
-      pb[nt] = as_frag(w);
-      lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nt], lacc[nt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
-    // O^T += V^T P^T with V^T fragments from transposing LDS reads
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
+    const float off0 = si.bias[0] - mu;
+    const float off1 = si.bias[NBLK - 1] - mu;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r] * a.scale_log2 + (r < 8 ? off0 : off1));
+    l_run += (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
+             (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+    // P^T B operand of key chunk c: keys 16c + 8(e/4) + 4hf + e%4 = registers 8c + e
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint4 w;
+      w.x = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
+      w.y = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
+      w.z = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
+      w.w = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
+      pb[c] = as_frag(w);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const unsigned char* vp = tv + (va ^ (uint32_t)(dt * 32));
-      const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
-      const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vp + 8 * D));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      bf16x8 vf[2];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        o[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[nt], o[dt][nt], 0, 0, 0);
+      for (int c = 0; c < 2; ++c) {
+        const unsigned char* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
+        const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
+        const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
+        vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], pb[c], o[dt], 0, 0, 0);
     }
   };
 
-  // ---- pipeline: sub-tile u computed from buffer u&1 while u+2 loads ----
+  // ---- pipeline: one barrier per sub-tile ----
+  // step u: wait for this wave's loads of sub-tile u, barrier (everyone's data
+  // of u is in buffer u&1 and buffer (u+1)&1 is no longer read), start loading
+  // sub-tile u+1 into buffer (u+1)&1, compute sub-tile u.
+  SubInfo si_cur;
   if (nsub > 0) {
-    stage(0);
-    commit(0);
-    if (nsub > 1) stage(1);
+    si_cur = info(0);
+    load_tiles(si_cur, 0);
+  }
+  for (int u = 0; u < nsub; ++u) {
+    const int b = u & 1;
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    SubInfo si_next;
+    if (u + 1 < nsub) {
+      si_next = info(u + 1);
+      load_tiles(si_next, b ^ 1);
+    }
+    compute(si_cur, b);
+    si_cur = si_next;
   }
   __syncthreads();
-  for (int u = 0; u < nsub; ++u) {
-    const int buf = u & 1;
-    // sub-tile u+1 (staged during the previous step) -> the other buffer;
-    // then start loading sub-tile u+2 while this one is computed
-    if (u + 1 < nsub) {
-      commit(buf ^ 1);
-      if (u + 2 < nsub) stage(u + 2);
-    }
-    compute(u, buf);
-    __syncthreads();   // buffer `buf` is rewritten two steps later; buf^1 is complete for step u+1
-  }
 
   // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
-  float* ostage = reinterpret_cast<float*>(tiles) + wave * RW * OS;
+  const float l = add_xor32(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* ostage = reinterpret_cast<float*>(tiles) + wave * 32 * OS;
+  // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float l = lacc[nt][0];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(ostage + (nt * 16 + col) * OS + dt * 16 + 4 * grp) = o[dt][nt] * inv;
-    if (grp == 0 && a.lse) {
-      const int64_t row = q0 + nt * 16 + col;
-      const float mu = m_run[nt] == -INFINITY ? 0.0f : m_run[nt];
-      if (row < a.seq_alloc)
-        a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
-    }
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<f32x4*>(ostage + qc * OS + 32 * dt + 8 * r4 + 4 * hf) =
+          f32x4{o[dt][4 * r4], o[dt][4 * r4 + 1], o[dt][4 * r4 + 2], o[dt][4 * r4 + 3]} * inv;
+  if (hf == 0 && a.lse) {
+    const int64_t row = q0 + qc;
+    const float mu = m_run == -INFINITY ? 0.0f : m_run;
+    if (row < a.seq_alloc)
+      a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
   }
   __syncthreads();
   T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
   constexpr int C8 = D / 8;
-  for (int e = lane; e < RW * C8; e += 64) {
+  for (int e = lane; e < 32 * C8; e += 64) {
     const int q = e / C8, c8 = e % C8;
     const int64_t row = q0 + q;
     if (row >= a.seq_alloc) continue;
@@ -466,10 +465,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 template <typename T, int D, int QROWS>
 hipError_t launch_bk(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.BH * a.nqb));
+  const dim3 block(QROWS * 2);
   switch (a.k_block) {
-    case 16: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 16>), grid, dim3(kFwdThreads), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 32>), grid, dim3(kFwdThreads), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 64>), grid, dim3(kFwdThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 16>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 32>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 64>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
