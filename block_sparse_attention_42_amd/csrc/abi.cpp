@@ -251,6 +251,15 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
   a.k_block = g->k_block;
   const float scale = softmax_scale > 0.0f ? softmax_scale : (float)(1.0 / std::sqrt((double)g->head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.dense_first = d.f0_first;
+  a.dense_last = d.f0_last;
+  const int64_t tpf = (int64_t)g->latent_h * g->latent_w;
+  a.period = tpf > 0 ? (int32_t)std::max<int64_t>(1, (tpf + g->q_block / 2) / g->q_block) : 1;
+  const int32_t nd = d.f0_first >= 0 ? d.f0_last - d.f0_first + 1 : 0;
+  a.n_dense = a.BH * nd;
+  const int64_t n_other = (int64_t)a.BH * (d.nqb - nd);
+  a.per_xcd = (int32_t)((n_other + bsa::kXcds - 1) / bsa::kXcds);
+  if (bsa::forward_grid(a) > 0x7fffffffLL) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
   hipError_t e = bsa::launch_forward(a, dtype, g->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();

@@ -57,7 +57,20 @@ struct FwdArgs {
   int64_t S;
   int32_t BH, nqb, nkb, q_block, k_block;
   float scale_log2;   // softmax scale * log2(e)
+  // launch schedule (performance only; every (head, query block) runs once)
+  int32_t dense_first, dense_last;   // frame-0 query blocks, run first (-1, -1: none)
+  int32_t period;                    // query blocks per frame, rounded (>= 1)
+  int32_t per_xcd;                   // remaining work items per XCD
+  int32_t n_dense;                   // BH * dense rows
 };
+
+// Work items of the forward launch: the frame-0 (longest) rows of every head
+// first, dealt round-robin over the XCDs, then the other rows in contiguous
+// per-XCD runs of consecutive work items (head-major; inside a head, query
+// blocks at the same in-frame position of successive frames are adjacent), so
+// that rows running together on one XCD share key blocks in its L2.
+constexpr int kXcds = 8;
+inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int64_t)kXcds * a.per_xcd; }
 
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);

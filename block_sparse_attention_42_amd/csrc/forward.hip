@@ -154,6 +154,39 @@ __device__ __forceinline__ int swz_v(int r) {
   else return 4 * ((r >> 1) & 1);
 }
 
+// blockIdx -> (head, query block); false for the few padding workgroups.
+__device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& qb) {
+  if (t < a.n_dense) {
+    bh = t % a.BH;
+    qb = a.dense_first + t / a.BH;
+    return true;
+  }
+  const int nd = a.dense_first >= 0 ? a.dense_last - a.dense_first + 1 : 0;
+  const int ns = a.nqb - nd;                       // other rows per head
+  const int x = t % kXcds, k = t / kXcds;
+  const int k0 = (a.n_dense + kXcds - 1 - x) / kXcds;
+  const int ls = x * a.per_xcd + (k - k0);         // rank among the other rows
+  if (ls >= a.BH * ns) return false;
+  bh = ls / ns;
+  const int r = ls % ns;
+  // r-th row of the head when rows are ordered by (index mod period, index)
+  const int P = a.period;
+  const int c = (ns + P - 1) / P;
+  const int m = ns % P == 0 ? P : ns % P;          // residues with c rows; the rest have c - 1
+  int res, kk;
+  if (r < m * c) {
+    res = r / c;
+    kk = r % c;
+  } else {
+    const int r2 = r - m * c;
+    res = m + r2 / (c - 1);
+    kk = r2 % (c - 1);
+  }
+  const int s = res + kk * P;
+  qb = (a.dense_first < 0 || s < a.dense_first) ? s : s + nd;
+  return true;
+}
+
 template <typename T, int D, int QROWS, int BK>
 __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   constexpr bool kDma = sizeof(T) == 2;  // bf16 tiles go HBM -> LDS directly; f32 is converted in registers
@@ -182,9 +215,8 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   const int qc = lane & 31;            // query column of S^T / O^T, A-operand row
   const int hf = lane >> 5;            // 0/1: K half of the operands, row half of the accumulators
 
-  // heaviest-first order: all heads of query block 0, then of block 1, ...
-  const int bh = blockIdx.x % a.BH;
-  const int qb = blockIdx.x / a.BH;
+  int bh, qb;
+  if (!schedule(a, blockIdx.x, bh, qb)) return;
   const int64_t rowid = (int64_t)bh * a.nqb + qb;
   const int cnt = min(max(a.cnt[rowid], 0), a.nkb);   // a row never reads past its nkb slots
   const int32_t* list = a.idx + rowid * a.nkb;
@@ -464,7 +496,7 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
 
 template <typename T, int D, int QROWS>
 hipError_t launch_bk(const FwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.BH * a.nqb));
+  const dim3 grid((unsigned)forward_grid(a));
   const dim3 block(QROWS * 2);
   switch (a.k_block) {
     case 16: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 16>), grid, block, 0, stream, a); break;

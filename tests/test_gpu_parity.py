@@ -62,8 +62,14 @@ def run_gpu(w, q, k, v, want_lse=True):
     qp = bsa.bsa_pool_blocks(qd, g, g.q_block)
     kp = bsa.bsa_pool_blocks(kd, g, g.k_block)
     mask, cnt, idx, logw = bsa.bsa_build_mask(qp, kp, g, _mp(w))
-    out, lse = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, want_lse=want_lse)
+    # NaN-filled outputs: every row (valid or pad) must be written by the kernel
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.H, w.seq_alloc), float("nan"), device=qd.device) if want_lse else None
+    out, lse = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, out=out, lse=lse)
     torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "forward left output rows unwritten"
+    if lse is not None:
+        assert not torch.isnan(lse).any().item(), "forward left LSE rows unwritten"
     r = dict(qp=qp.cpu().numpy(), kp=kp.cpu().numpy(), mask=mask.cpu().numpy().astype(bool),
              cnt=cnt.cpu().numpy(), idx=idx.cpu().numpy(),
              logw=None if logw is None else logw.cpu().numpy(),
