@@ -32,7 +32,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kListCap = 2048;     // list entries of a row cached in LDS (the rest read from global)
 
 template <typename T>
 struct Ld8;
@@ -125,6 +124,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 
 // x combined with the same register of lane ^ 32 (one v_permlane32_swap).
@@ -188,7 +188,7 @@ __device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& 
 }
 
 template <typename T, int D, int QROWS, int BK>
-__global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(QROWS * 2, QROWS == 64 ? 2 : 1) void fwd_kernel(FwdArgs a) {
   constexpr bool kDma = sizeof(T) == 2;  // bf16 tiles go HBM -> LDS directly; f32 is converted in registers
   constexpr int NW = QROWS / 32;       // waves: each owns 32 query rows
   constexpr int NTH = NW * 64;         // threads
@@ -207,11 +207,10 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   constexpr int kTileHalves = 4 * TILE_E;          // K0, V0, K1, V1 (bf16 units)
   constexpr int kStageHalves = QROWS * OS * 2;     // output staging (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[kTileHalves > kStageHalves ? kTileHalves : kStageHalves];
-  __shared__ uint16_t lst[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int qc = lane & 31;            // query column of S^T / O^T, A-operand row
   const int hf = lane >> 5;            // 0/1: K half of the operands, row half of the accumulators
 
@@ -229,29 +228,18 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   const int64_t q0 = (int64_t)qb * a.q_block + wave * 32;     // this wave's first row
   const int S32 = (int)a.S;
 
-  // ---- the row's block list in LDS (entries past kListCap read from global) ----
-  for (int e = tid; e < min(cnt, kListCap); e += NTH) {
-    const int j = list[e];
-    lst[e] = (j >= 0 && j < a.nkb) ? (uint16_t)j : (uint16_t)0xffff;
-  }
-  __syncthreads();
-  auto block_at = [&](int pos) -> int {          // -1: past the list or a bad index
-    int j = -1;
-    if (pos < cnt) {
-      if (pos < kListCap) {
-        j = lst[pos];
-        j = j == 0xffff ? -1 : j;
-      } else {
-        j = list[pos];
-        j = (j >= 0 && j < a.nkb) ? j : -1;
-      }
-    }
-    return __builtin_amdgcn_readfirstlane(j);     // wave-uniform
-  };
-  // log2-domain weight of list slot pos (uniform load; only in weighted calls)
-  auto bias_at = [&](int pos) -> float {
-    if (!lw) return 0.0f;
-    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(lw[pos]))) * 1.4426950408889634f;
+  // block index of list slot pos (-1 past the list or for a bad index) and its
+  // log2-domain weight.  The lists are read-only for the whole launch, so they
+  // are read through the constant address space: uniform indices become scalar
+  // loads that never wait on the tile loads in flight.
+  typedef const __attribute__((address_space(4))) int32_t* cint_p;
+  typedef const __attribute__((address_space(4))) float* cflt_p;
+  const cint_p lst = (cint_p)list;
+  const cflt_p lwr = (cflt_p)lw;
+  auto block_at = [&](int pos) -> int {
+    if (pos >= cnt) return -1;
+    const int j = lst[pos];
+    return (j >= 0 && j < a.nkb) ? j : -1;
   };
 
   const uint32_t nbytes = (uint32_t)a.seq_alloc * (uint32_t)D * (uint32_t)sizeof(T);
@@ -304,22 +292,37 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
   // ---- sub-tile geometry: first key, valid keys and log2 weight of each part ----
+  // The raw list entries of a sub-tile are fetched (scalar loads) one step
+  // before they are turned into its geometry, so the loads never stall a step.
+  struct Raw {
+    int j[NBLK];
+    float w[NBLK];
+  };
   struct SubInfo {
     int key0[NBLK];      // first key of each part (0 if none)
     int valid[NBLK];     // valid keys of each part
     float bias[NBLK];
   };
-  auto info = [&](int u) {
+  auto fetch = [&](int u) {
+    Raw r;
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) {
+      const int pos = (u * SUB + b * PART) / BK;
+      r.j[b] = block_at(pos);
+      r.w[b] = (pos < cnt && lwr) ? lwr[pos] : 0.0f;
+    }
+    return r;
+  };
+  auto make_info = [&](int u, const Raw& r) {
     SubInfo si;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int g = u * SUB + b * PART;
-      const int pos = g / BK;
-      const int j = block_at(pos);
+      const int j = r.j[b];
       const int key0 = j * BK + g % BK;
       si.key0[b] = j >= 0 ? key0 : 0;
       si.valid[b] = j >= 0 ? min(max(S32 - key0, 0), PART) : 0;
-      si.bias[b] = j >= 0 ? bias_at(pos) : 0.0f;
+      si.bias[b] = j >= 0 ? r.w[b] * 1.4426950408889634f : 0.0f;
     }
     return si;
   };
@@ -330,19 +333,32 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   // ---- a sub-tile's K and V rows -> LDS buffer b ----
   uint4 kst[kDma ? 1 : NLD], vst[kDma ? 1 : NLD];   // f32 only: staged in registers
   auto load_tiles = [&](const SubInfo& si, int b) {
+    bool full = true;
+#pragma unroll
+    for (int p = 0; p < NBLK; ++p) full = full && si.valid[p] == PART;
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int part = (n * RPL) / PART;
       const bool ok = rin[n] < si.valid[part];
       const uint32_t base = (uint32_t)si.key0[part] * (uint32_t)D;
       if constexpr (kDma) {
-        // this wave's 64 lanes fill 1 KB of LDS at chunk n*NTH + 64*wave
-        const uint32_t kb = ok ? (base + kc[n]) * 2u : kOob;
-        const uint32_t vb = ok ? (base + vc[n]) * 2u : kOob;
+        // this wave's 64 lanes fill 1 KB of LDS at chunk n*NTH + 64*wave.  A full
+        // sub-tile adds the uniform block base as soffset to constant voffsets;
+        // otherwise invalid rows get an out-of-range voffset (the load writes zeros).
+        uint32_t kv, vv, so;
+        if (full) {
+          kv = kc[n] * 2u;
+          vv = vc[n] * 2u;
+          so = base * 2u;
+        } else {
+          kv = ok ? (base + kc[n]) * 2u : kOob;
+          vv = ok ? (base + vc[n]) * 2u : kOob;
+          so = 0;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)kb, 0, 0, 0);
+            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)kv, (int)so, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)vb, 0, 0, 0);
+            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)vv, (int)so, 0, 0);
       } else {
         kst[n] = BufLd8<T>::load(rk, ok ? base + kc[n] : kOob);
         vst[n] = BufLd8<T>::load(rv, ok ? base + vc[n] : kOob);
@@ -381,9 +397,12 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
         if (row - p * PART >= si.valid[p]) sc[r] = -INFINITY;
       }
     }
-    // row max: the lane's 16 keys, then lane ^ 32 (scale > 0, one weight per part)
-    const float mx0 = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    const float mx1 = fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])), fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15])));
+    // row max: the lane's 16 keys (v_max3 chains), then lane ^ 32 (scale > 0,
+    // one weight per part)
+    const float mx0 = fmaxf(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), sc[2]), fmaxf(sc[3], sc[4])),
+                            fmaxf(fmaxf(sc[5], sc[6]), sc[7]));
+    const float mx1 = fmaxf(fmaxf(fmaxf(fmaxf(sc[8], sc[9]), sc[10]), fmaxf(sc[11], sc[12])),
+                            fmaxf(fmaxf(sc[13], sc[14]), sc[15]));
     float mx;
     if constexpr (NBLK == 2) mx = fmaxf(mx0 * a.scale_log2 + si.bias[0], mx1 * a.scale_log2 + si.bias[1]);
     else mx = fmaxf(mx0, mx1) * a.scale_log2 + si.bias[0];
@@ -404,19 +423,21 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r] * a.scale_log2 + (r < 8 ? off0 : off1));
-    l_run += (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
-             (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
-    // P^T B operand of key chunk c: keys 16c + 8(e/4) + 4hf + e%4 = registers 8c + e
+    // P^T B operand of key chunk c: keys 16c + 8(e/4) + 4hf + e%4 = registers 8c + e;
+    // the row sum adds exactly these bf16 values (v_dot2 with ones)
     bf16x8 pb[2];
+    float ps = 0.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      uint4 w;
-      w.x = pack_bf16x2(p[8 * c + 0], p[8 * c + 1]);
-      w.y = pack_bf16x2(p[8 * c + 2], p[8 * c + 3]);
-      w.z = pack_bf16x2(p[8 * c + 4], p[8 * c + 5]);
-      w.w = pack_bf16x2(p[8 * c + 6], p[8 * c + 7]);
-      pb[c] = as_frag(w);
+      uint32_t w[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        w[k2] = pack_bf16x2(p[8 * c + 2 * k2], p[8 * c + 2 * k2 + 1]);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k2]), kOnes2, ps, false);
+      }
+      pb[c] = as_frag(make_uint4(w[0], w[1], w[2], w[3]));
     }
+    l_run += ps;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       bf16x8 vf[2];
@@ -438,9 +459,11 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
   // of u is in buffer u&1 and buffer (u+1)&1 is no longer read), start loading
   // sub-tile u+1 into buffer (u+1)&1, compute sub-tile u.
   SubInfo si_cur;
+  Raw raw_next;
   if (nsub > 0) {
-    si_cur = info(0);
+    si_cur = make_info(0, fetch(0));
     load_tiles(si_cur, 0);
+    if (nsub > 1) raw_next = fetch(1);
   }
   for (int u = 0; u < nsub; ++u) {
     const int b = u & 1;
@@ -448,8 +471,9 @@ __global__ __launch_bounds__(QROWS * 2, 2) void fwd_kernel(FwdArgs a) {
     __syncthreads();
     SubInfo si_next;
     if (u + 1 < nsub) {
-      si_next = info(u + 1);
+      si_next = make_info(u + 1, raw_next);
       load_tiles(si_next, b ^ 1);
+      if (u + 2 < nsub) raw_next = fetch(u + 2);
     }
     compute(si_cur, b);
     si_cur = si_next;
