@@ -33,7 +33,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan_1p3b_keep10")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-qblocks", type=int, default=1024)
+    ap.add_argument("--cpu-sample-qblocks", type=int, default=512)
+    ap.add_argument("--cpu-sample-heads", type=int, default=3)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -51,9 +52,10 @@ def _traffic(path_src, name):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, nblocks):
-    """The oracle, as it stands, on one head: pooling and the mask of every
-    row, then token-expanded attention of `nblocks` query blocks."""
+def cpu_baseline(w, q, k, v, nblocks, nheads):
+    """The oracle, as it stands, on the first `nheads` heads: per head, pooling
+    and the mask of every row, then token-expanded attention of `nblocks`
+    query blocks (the frame-0 rows among them)."""
     import numpy as np
     import oracle
     try:
@@ -65,27 +67,31 @@ def cpu_baseline(w, q, k, v, nblocks):
                         w.seq_alloc)
     p = oracle.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio, frame0_dense=w.frame0_dense,
                           text_columns=w.text_columns, log_cluster=w.log_cluster, seed=w.sample_seed)
-    q1, k1, v1 = q[:1, :1], k[:1, :1], v[:1, :1]
-    rng = np.random.default_rng(0)
-    f0 = list(g.frame0_q_blocks())
-    qbl = sorted(set(f0[:max(1, nblocks // 10)]) |
-                 set(rng.choice(g.nqb, nblocks, replace=False).tolist()))[:nblocks]
-    t0 = time.perf_counter()
-    qp = oracle.pool_blocks(q1, g.S, g.q_block)
-    kp = oracle.pool_blocks(k1, g.S, g.k_block)
-    _, cnt, idx, logw = oracle.build_mask(qp, kp, g, p)
-    t1 = time.perf_counter()
-    oracle.attention_head(q1[0, 0], k1[0, 0], v1[0, 0], g, cnt[0, 0], idx[0, 0], logw[0, 0], q_blocks=qbl)
-    t2 = time.perf_counter()
-    flops = 4.0 * w.D * w.q_block * w.k_block * float(cnt[0, 0, qbl].sum())
-    # the sampled q-blocks' share of one head's mask work is charged to them
-    mask_share = (t1 - t0) * len(qbl) / g.nqb
-    sec = (t2 - t1) + mask_share
+    nheads = max(1, min(nheads, w.H))
+    nblocks = max(1, min(nblocks, g.nqb))
+    flops = sec = wall = 0.0
+    for h in range(nheads):
+        q1, k1, v1 = q[:1, h:h + 1], k[:1, h:h + 1], v[:1, h:h + 1]
+        rng = np.random.default_rng(h)
+        f0 = list(g.frame0_q_blocks())
+        qbl = sorted(set(f0[:max(1, nblocks // 10)]) |
+                     set(rng.choice(g.nqb, nblocks, replace=False).tolist()))[:nblocks]
+        t0 = time.perf_counter()
+        qp = oracle.pool_blocks(q1, g.S, g.q_block)
+        kp = oracle.pool_blocks(k1, g.S, g.k_block)
+        _, cnt, idx, logw = oracle.build_mask(qp, kp, g, p)
+        t1 = time.perf_counter()
+        oracle.attention_head(q1[0, 0], k1[0, 0], v1[0, 0], g, cnt[0, 0], idx[0, 0], logw[0, 0], q_blocks=qbl)
+        t2 = time.perf_counter()
+        flops += 4.0 * w.D * w.q_block * w.k_block * float(cnt[0, 0, qbl].sum())
+        # the sampled q-blocks' share of one head's mask work is charged to them
+        sec += (t2 - t1) + (t1 - t0) * len(qbl) / g.nqb
+        wall += t2 - t0
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"head 0 of {w.name}: pooling + mask of all {g.nqb} rows (charged pro rata) and "
-                      f"float64 token-expanded attention of {len(qbl)} query blocks "
-                      f"({(t2 - t0):.1f} s wall)",
-            "seconds": round(t2 - t0, 2)}
+            "sample": f"heads 0..{nheads - 1} of {w.name}: per head, pooling + mask of all {g.nqb} rows "
+                      f"(charged pro rata) and float64 token-expanded attention of {nblocks} query blocks "
+                      f"({wall:.1f} s wall)",
+            "seconds": round(wall, 2)}
 
 
 def main():
@@ -205,7 +211,7 @@ def main():
                      "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks, a.cpu_sample_heads)
     res["input_gen_s"] = round(t_gen, 1)
     print(json.dumps(res), flush=True)
 
