@@ -6,96 +6,87 @@
 // reweighting) and "Attention matrix view: make only frame-0 query rows
 // dense" (sec. 2: a dense row attends to every key/value token).
 //
-// Work decomposition (CDNA4-first):
-//   * one workgroup = one (b, h, query block) of QROWS rows, 4 waves;
-//   * the row's selected key blocks are cut into 64-key tiles (64/BK blocks
-//     per tile, so 16-key blocks are gathered four per tile), and the tiles
-//     are dealt round-robin to the 4 waves; every wave keeps all QROWS rows,
-//     so no K/V tile is shared between waves and the only cross-wave step is
-//     one log-sum-exp merge at the end;
-//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (float32
-//     accumulate).  Computing the transposes keeps each query row in a fixed
-//     lane (lane & 15) for S, P and O alike, so the online-softmax state
-//     (running max, partial sum, rescale) never moves between lanes;
-//   * K rows are loaded straight from HBM/L2 into the A-operand registers
-//     (16 bytes per lane), in a permuted order chosen so that the P^T
-//     B-operand of each lane covers 8 consecutive keys; V goes through a
-//     per-wave LDS tile that is read back transposed;
-//   * softmax in the log2 domain (exp2 on the hardware transcendental),
-//     scale and per-block log-weight folded into one multiply-add.
+// Work decomposition:
+//   * one workgroup = one wave = one (b, h, query block) of 32 or 64 rows.
+//     The wave may use up to 512 registers (one wave per SIMD), so the O^T
+//     accumulators and Q fragments of the whole query block, two score
+//     tiles and two key sub-tiles stay in registers, and every K/V byte read
+//     from LDS or L2 feeds all rows of the block;
+//   * the block's selected key blocks are walked in 32-key sub-tiles
+//     (16-key blocks are gathered two per sub-tile);
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: each lane
+//     owns one query column of a 32-row tile, so the running max, sum and
+//     rescale stay in the lane (one permlane32 swap joins the key halves);
+//   * K rows go from L2 straight into A-operand registers (16 bytes per lane
+//     per k chunk, no LDS), issued three sub-tiles ahead; V rows go to LDS by
+//     buffer-load DMA into a three-deep ring, issued two sub-tiles ahead, and
+//     are read back with the transposing LDS read as V^T A operands;
+//   * software pipeline per sub-tile u: the S(u+1) MFMAs are interleaved with
+//     the exponentials of S(u), and the P V MFMAs of u with the row max of
+//     S(u+1), so matrix cores and vector ALU overlap inside the wave;
+//   * softmax in the log2 domain with lazy rescaling (the reference max moves
+//     only when a row max grows by more than 8), scale and per-block
+//     log-weight folded into one multiply-add.
 #include "bsa_internal.h"
 
 namespace bsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
-
-template <typename T>
-struct Ld8;
-
-template <>
-struct Ld8<bf16_t> {
-  static __device__ __forceinline__ uint4 raw(const bf16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-};
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr uint32_t kOob = 0x80000000u;   // byte offset past any buffer: the load returns zeros
 
 // Two floats as two bf16 (round to nearest even) in one dword: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-
-template <>
-struct Ld8<float> {
-  static __device__ __forceinline__ uint4 raw(const float* p) {
-    const float4 x = reinterpret_cast<const float4*>(p)[0];
-    const float4 y = reinterpret_cast<const float4*>(p)[1];
-    uint4 r;
-    r.x = pack_bf16x2(x.x, x.y);
-    r.y = pack_bf16x2(x.z, x.w);
-    r.z = pack_bf16x2(y.x, y.y);
-    r.w = pack_bf16x2(y.z, y.w);
-    return r;
-  }
-};
 
 __device__ __forceinline__ bf16x8 as_frag(uint4 r) { return __builtin_bit_cast(bf16x8, r); }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOob = 0x80000000u;   // byte offset past any buffer: the load returns zeros
+__device__ __forceinline__ uint4 pack8(u32x4 x, u32x4 y) {
+  uint4 o;
+  o.x = pack_bf16x2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  o.y = pack_bf16x2(__uint_as_float(x[2]), __uint_as_float(x[3]));
+  o.z = pack_bf16x2(__uint_as_float(y[0]), __uint_as_float(y[1]));
+  o.w = pack_bf16x2(__uint_as_float(y[2]), __uint_as_float(y[3]));
+  return o;
+}
 
-// Range-checked loads of 8 consecutive elements (as 8 bf16) through a buffer
-// resource; an offset >= the resource size reads zeros, so invalid key rows
-// need no branch.
+// 8 consecutive elements of a row as 8 bf16 (float rows are rounded).
 template <typename T>
-struct BufLd8;
+struct Row8;
 
 template <>
-struct BufLd8<bf16_t> {
-  static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, uint32_t elem_off) {
-    const uint32_t byte = elem_off == kOob ? kOob : elem_off * 2u;
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte, 0, 0);
+struct Row8<bf16_t> {
+  static constexpr int kOps = 1;   // buffer loads per 8 elements
+  static __device__ __forceinline__ uint4 ld(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  static __device__ __forceinline__ uint4 buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
   }
 };
 
 template <>
-struct BufLd8<float> {
-  static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, uint32_t elem_off) {
-    const uint32_t byte = elem_off == kOob ? kOob : elem_off * 4u;
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte, 0, 0);
-    const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(byte == kOob ? kOob : byte + 16u), 0, 0);
-    uint4 o;
-    o.x = pack_bf16x2(__uint_as_float(x[0]), __uint_as_float(x[1]));
-    o.y = pack_bf16x2(__uint_as_float(x[2]), __uint_as_float(x[3]));
-    o.z = pack_bf16x2(__uint_as_float(y[0]), __uint_as_float(y[1]));
-    o.w = pack_bf16x2(__uint_as_float(y[2]), __uint_as_float(y[3]));
-    return o;
+struct Row8<float> {
+  static constexpr int kOps = 2;
+  static __device__ __forceinline__ uint4 ld(const float* p) {
+    const float4 x = reinterpret_cast<const float4*>(p)[0];
+    const float4 y = reinterpret_cast<const float4*>(p)[1];
+    return pack8(u32x4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)},
+                 u32x4{__float_as_uint(y.x), __float_as_uint(y.y), __float_as_uint(y.z), __float_as_uint(y.w)});
+  }
+  static __device__ __forceinline__ uint4 buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16u), (int)soff, 0);
+    return pack8(x, y);
   }
 };
 
@@ -120,13 +111,6 @@ __device__ __forceinline__ void store8<float>(float* dst, const float (&v)[8]) {
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-
 // x combined with the same register of lane ^ 32 (one v_permlane32_swap).
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -137,17 +121,37 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS chunk swizzles of the 32-row K and V sub-tiles (16-byte chunks of a row
-// of D bf16).  K rows are read as 16-byte A-operand pieces, 16 consecutive
-// rows at the same logical chunk per access; V rows are read with the
-// transposing 8-byte load, 4 consecutive rows x 4 chunks per 16 lanes.  The
-// XOR patterns put each access group on distinct banks; they only touch chunk
-// bits, so every address is (lane base) ^ (per-fragment constant).
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return (r >> 1) & 7;
+// ---- matrix instructions with fixed register files ----
+// The score tiles S^T are produced by MFMAs and consumed by vector code, so
+// they live in VGPRs; the O^T accumulators and the Q fragments are only ever
+// MFMA operands and live in AGPRs.  The compiler cannot be told that per
+// instruction, so these MFMAs are written as inline assembly with register
+// class constraints.  Because the compiler does not see them as MFMAs, the
+// code around them keeps the hardware's wait-state rules itself: a vector
+// write of an MFMA source needs 2 wait states before the MFMA, and a vector
+// read of an MFMA result needs 12 after it (8-pass 32x32x16).
+__device__ __forceinline__ void mma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b) : "memory");
 }
+__device__ __forceinline__ void mma_s(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b) : "memory");
+}
+__device__ __forceinline__ void mma_o(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b) : "memory");
+}
+// The "memory" clobber keeps every memory instruction (tile loads, LDS reads)
+// where the source puts it relative to these MFMAs.
+// Empty ordering points: work reading x is placed after (pin_after), work
+// producing x before (pin_before), relative to the neighbouring asm.
+template <typename X>
+__device__ __forceinline__ void pin_after(X& x) { asm volatile("" : "+v"(x)); }
+template <typename X>
+__device__ __forceinline__ void pin_before(const X& x) { asm volatile("" ::"v"(x)); }
+
+// LDS chunk swizzle of a 32-row V sub-tile (16-byte chunks of a row of D
+// bf16).  V is read with the transposing 8-byte load, 4 consecutive rows x 4
+// chunks per 16 lanes; the XOR puts each such group on distinct banks and only
+// touches chunk bits, so every read address is (lane base) ^ (constant).
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
   if constexpr (D == 128) return 4 * (r & 3);
@@ -187,134 +191,104 @@ __device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& 
   return true;
 }
 
-template <typename T, int D, int QROWS, int BK>
-__global__ __launch_bounds__(QROWS * 2, QROWS == 64 ? 2 : 1) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, int QT, int BK>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(1, 1)))
+void fwd_kernel(FwdArgs a) {
   constexpr bool kDma = sizeof(T) == 2;  // bf16 tiles go HBM -> LDS directly; f32 is converted in registers
-  constexpr int NW = QROWS / 32;       // waves: each owns 32 query rows
-  constexpr int NTH = NW * 64;         // threads
-  constexpr int KC = D / 16;           // K-chunks of the Q.K contraction (32x32x16)
+  constexpr uint32_t ES = sizeof(T);
+  constexpr uint32_t RB = D * ES;      // bytes per K/V row in memory
+  constexpr int KC = D / 16;           // k chunks of the Q.K contraction (32x32x16)
   constexpr int DT = D / 32;           // d tiles of O^T
-  constexpr int KCH = D / 8;           // 16-byte chunks per row
+  constexpr int KCH = D / 8;           // 16-byte (8 x bf16) chunks per row
   constexpr int SUB = 32;              // keys per sub-tile
-  constexpr int TILE_E = SUB * D;      // bf16 elements of one K (or V) sub-tile
-  constexpr int NLD = SUB * KCH / NTH; // 16-byte loads per thread per operand
-  constexpr int RPL = NTH / KCH;       // tile rows covered by one load round
+  constexpr int TILE_E = SUB * D;      // bf16 elements of one K or V sub-tile in LDS
+  constexpr int NLD = SUB * KCH / 64;  // chunks per lane per sub-tile
+  constexpr int RPL = 64 / KCH;        // sub-tile rows per load round
   constexpr int NBLK = BK >= SUB ? 1 : SUB / BK;   // key blocks per sub-tile
   constexpr int PART = SUB / NBLK;
-  constexpr int OS = D + 4;            // LDS row stride of the output staging (floats)
   constexpr float kTau = 8.0f;         // lazy rescale: tolerated growth of the running max (log2)
-  static_assert(NW >= 1 && NLD >= 1 && NBLK <= 2, "tile shape");
-  constexpr int kTileHalves = 4 * TILE_E;          // K0, V0, K1, V1 (bf16 units)
-  constexpr int kStageHalves = QROWS * OS * 2;     // output staging (bf16 units)
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[kTileHalves > kStageHalves ? kTileHalves : kStageHalves];
+  constexpr int LOPS = NLD * (kDma ? 1 : Row8<T>::kOps);   // VMEM instructions per tile
+  static_assert(NBLK <= 2 && PART % RPL == 0 && NLD >= 1, "tile shape");
+  // One LDS array per ring slot: the compiler then knows which tile loads a
+  // read can depend on, and never waits for the loads still in flight into
+  // the other slots.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_E], k_lds1[TILE_E];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_E], v_lds1[TILE_E];
+  // destination of the tile loads of a step whose tile is loaded separately
+  // (partial tiles): the instructions still run, their data is discarded
+  __shared__ __attribute__((aligned(16))) uint16_t sink_lds[64 * 8];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int qc = lane & 31;            // query column of S^T / O^T, A-operand row
-  const int hf = lane >> 5;            // 0/1: K half of the operands, row half of the accumulators
+  const int lane = threadIdx.x;
+  const int qc = lane & 31;            // query column of S^T / O^T, key row of the K operand
+  const int hf = lane >> 5;            // 0/1: k half of the operands, row half of the accumulators
 
   int bh, qb;
   if (!schedule(a, blockIdx.x, bh, qb)) return;
   const int64_t rowid = (int64_t)bh * a.nqb + qb;
-  const int cnt = min(max(a.cnt[rowid], 0), a.nkb);   // a row never reads past its nkb slots
-  const int32_t* list = a.idx + rowid * a.nkb;
-  const float* lw = a.logw ? a.logw + rowid * a.nkb : nullptr;
+  // (read-first-lane: row values are wave-uniform and should live in scalar registers)
+  const int cnt = __builtin_amdgcn_readfirstlane(min(max(a.cnt[rowid], 0), a.nkb));   // never past nkb slots
   const int nsub = (cnt * BK + SUB - 1) / SUB;          // 32-key sub-tiles of the row
 
   const T* Qb = reinterpret_cast<const T*>(a.q) + (int64_t)bh * a.seq_alloc * D;
   const T* Kb = reinterpret_cast<const T*>(a.k) + (int64_t)bh * a.seq_alloc * D;
   const T* Vb = reinterpret_cast<const T*>(a.v) + (int64_t)bh * a.seq_alloc * D;
-  const int64_t q0 = (int64_t)qb * a.q_block + wave * 32;     // this wave's first row
+  const int64_t q0 = (int64_t)qb * a.q_block;
   const int S32 = (int)a.S;
 
-  // block index of list slot pos (-1 past the list or for a bad index) and its
-  // log2-domain weight.  The lists are read-only for the whole launch, so they
-  // are read through the constant address space: uniform indices become scalar
-  // loads that never wait on the tile loads in flight.
+  // List entries are read-only for the whole launch: read them through the
+  // constant address space, so uniform indices become scalar loads.
   typedef const __attribute__((address_space(4))) int32_t* cint_p;
   typedef const __attribute__((address_space(4))) float* cflt_p;
-  const cint_p lst = (cint_p)list;
-  const cflt_p lwr = (cflt_p)lw;
-  auto block_at = [&](int pos) -> int {
-    if (pos >= cnt) return -1;
-    const int j = lst[pos];
-    return (j >= 0 && j < a.nkb) ? j : -1;
-  };
+  const cint_p lst = (cint_p)(a.idx + rowid * a.nkb);
+  const cflt_p lwr = a.logw ? (cflt_p)(a.logw + rowid * a.nkb) : nullptr;
 
-  const uint32_t nbytes = (uint32_t)a.seq_alloc * (uint32_t)D * (uint32_t)sizeof(T);
+  const uint32_t nbytes = (uint32_t)a.seq_alloc * RB;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Qb, 0, (int)nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, (int)nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, (int)nbytes, 0x00020000);
 
   // ---- Q^T fragments (B operand of S^T = K Q^T): Q[q][16c + 8hf .. +7] ----
-  bf16x8 qf[KC];
-  {
-    const int64_t row = q0 + qc;
+  // rows past S read zeros
+  bf16x8 qf[QT][KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      uint4 r = make_uint4(0, 0, 0, 0);
-      if (row < a.S) r = Ld8<T>::raw(Qb + row * D + c * 16 + hf * 8);
-      qf[c] = as_frag(r);
-    }
+  for (int qt = 0; qt < QT; ++qt) {
+    const int64_t row = q0 + 32 * qt + qc;
+    const uint32_t off = row < a.S ? (uint32_t)row * RB + (uint32_t)(8 * hf) * ES : kOob;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[qt][c] = as_frag(Row8<T>::buf(rq, off + (uint32_t)(16 * c) * ES, 0));
   }
-
-  // ---- per-thread constant offsets ----
-  // Tile load n of this thread fills LDS chunk n*NTH + tid: tile row
-  // r = n*RPL + tid/KCH, holding logical chunk (tid % KCH) ^ swizzle(r).  Its
-  // global element offset is key0(part) * D + (r - part*PART) * D + chunk*8,
-  // and the part of load n is the same for every thread.
-  int rin[NLD];
-  uint32_t kc[NLD], vc[NLD];
+  // Q is only ever an MFMA operand: keep it in the accumulation registers,
+  // leaving the vector registers to the score tiles and the softmax.
 #pragma unroll
-  for (int n = 0; n < NLD; ++n) {
-    const int r = n * RPL + tid / KCH;
-    rin[n] = r - ((n * RPL) / PART) * PART;
-    kc[n] = (uint32_t)(rin[n] * D + ((tid % KCH) ^ swz_k<D>(r)) * 8);
-    vc[n] = (uint32_t)(rin[n] * D + ((tid % KCH) ^ swz_v<D>(r)) * 8);
-  }
-  // K A-operand read of chunk c: tile row qc, logical chunk 2c + hf:
-  // byte address ka ^ (c * 32).
-  const uint32_t ka = (uint32_t)(qc * KCH * 16) | (uint32_t)((hf ^ swz_k<D>(qc)) * 16);
-  // V^T A-operand transposing reads: 16-lane group g = lane/16 covers d columns
-  // 16*(g & 1) + [0, 16) of d tile dt; lane i of the group addresses tile row
-  // 16c + 8hh + 4hf + i/4 and columns 32dt + 16(g & 1) + 4(i & 3):
-  // byte address va ^ (dt * 64) + (16c + 8hh) rows.
-  const uint32_t va = [&] {
-    const int i = lane & 15, g = lane >> 4;
-    const int r = 4 * hf + (i >> 2);
-    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
-    return (uint32_t)(r * D * 2) | (uint32_t)((lc ^ swz_v<D>(r)) * 16) | (uint32_t)((i & 1) * 8);
-  }();
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 o[DT];
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+    for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(qf[qt][c]));
 
   // ---- sub-tile geometry: first key, valid keys and log2 weight of each part ----
-  // The raw list entries of a sub-tile are fetched (scalar loads) one step
-  // before they are turned into its geometry, so the loads never stall a step.
   struct Raw {
     int j[NBLK];
     float w[NBLK];
   };
-  struct SubInfo {
+  struct Info {
     int key0[NBLK];      // first key of each part (0 if none)
-    int valid[NBLK];     // valid keys of each part
-    float bias[NBLK];
+    int valid[NBLK];     // valid keys of each part (0 if none)
+    float bias[NBLK];    // log2-domain weight of each part
   };
   auto fetch = [&](int u) {
     Raw r;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int pos = (u * SUB + b * PART) / BK;
-      r.j[b] = block_at(pos);
-      r.w[b] = (pos < cnt && lwr) ? lwr[pos] : 0.0f;
+      const int pc = min(pos, max(cnt - 1, 0));   // every row has nkb >= 1 slots
+      const int j = lst[pc];
+      r.j[b] = __builtin_amdgcn_readfirstlane((pos < cnt && j >= 0 && j < a.nkb) ? j : -1);
+      r.w[b] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                   __builtin_bit_cast(int, (pos < cnt && lwr) ? lwr[pc] : 0.0f)));
     }
     return r;
   };
-  auto make_info = [&](int u, const Raw& r) {
-    SubInfo si;
+  auto info = [&](int u, const Raw& r) {
+    Info si;
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int g = u * SUB + b * PART;
@@ -326,206 +300,498 @@ __global__ __launch_bounds__(QROWS * 2, QROWS == 64 ? 2 : 1) void fwd_kernel(Fwd
     }
     return si;
   };
-
-  auto kbuf = [&](int b) { return tiles + b * 2 * TILE_E; };
-  auto vbuf = [&](int b) { return tiles + b * 2 * TILE_E + TILE_E; };
-
-  // ---- a sub-tile's K and V rows -> LDS buffer b ----
-  uint4 kst[kDma ? 1 : NLD], vst[kDma ? 1 : NLD];   // f32 only: staged in registers
-  auto load_tiles = [&](const SubInfo& si, int b) {
+  auto is_full = [&](const Info& si) {
     bool full = true;
 #pragma unroll
     for (int p = 0; p < NBLK; ++p) full = full && si.valid[p] == PART;
-#pragma unroll
-    for (int n = 0; n < NLD; ++n) {
-      const int part = (n * RPL) / PART;
-      const bool ok = rin[n] < si.valid[part];
-      const uint32_t base = (uint32_t)si.key0[part] * (uint32_t)D;
-      if constexpr (kDma) {
-        // this wave's 64 lanes fill 1 KB of LDS at chunk n*NTH + 64*wave.  A full
-        // sub-tile adds the uniform block base as soffset to constant voffsets;
-        // otherwise invalid rows get an out-of-range voffset (the load writes zeros).
-        uint32_t kv, vv, so;
-        if (full) {
-          kv = kc[n] * 2u;
-          vv = vc[n] * 2u;
-          so = base * 2u;
-        } else {
-          kv = ok ? (base + kc[n]) * 2u : kOob;
-          vv = ok ? (base + vc[n]) * 2u : kOob;
-          so = 0;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(kbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)kv, (int)so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(vbuf(b) + (n * NTH + 64 * wave) * 8), 16, (int)vv, (int)so, 0, 0);
-      } else {
-        kst[n] = BufLd8<T>::load(rk, ok ? base + kc[n] : kOob);
-        vst[n] = BufLd8<T>::load(rv, ok ? base + vc[n] : kOob);
-      }
+    return full;
+  };
+
+  // ---- K / V sub-tile -> LDS ring slot ----
+  // Load n of this lane fills LDS chunk n*64 + lane of the slot: tile row
+  // r = n*RPL + lane/KCH, holding logical chunk (lane % KCH) ^ swizzle(r);
+  // all rows of one load round belong to one part.  Rows past the valid keys
+  // (or of a missing part) read zeros.
+  //   K rows are read back as 16-byte A-operand pieces, 16 consecutive rows
+  //   at one logical chunk per access: swizzle r & 15 (D = 128) or
+  //   (r >> 1) & 7 (D = 64) spreads them over the banks.
+  //   V rows are read with the transposing 8-byte load, 4 consecutive rows x 4
+  //   chunks per 16 lanes: swizzle 4(r & 3) (D = 128) or 4((r >> 1) & 1).
+  // Both swizzles only touch chunk bits, so every LDS read address is a lane
+  // base XOR a per-fragment constant.
+  const int vrow = lane / KCH;
+  auto swz_k = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto chunk_off = [&](int n, bool is_k) {
+    const int r = n * RPL + vrow;
+    return (uint32_t)(vrow * D + ((lane % KCH) ^ (is_k ? swz_k(r) : swz_v<D>(r))) * 8) * ES;
+  };
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  auto lds_frag = [](const lds_u8* p) {
+    const u32x4 v = *reinterpret_cast<const lds_u32x4*>(p);
+    return as_frag(make_uint4(v[0], v[1], v[2], v[3]));
+  };
+  auto kslot = [&](int s) { return s == 0 ? (lds_u16*)k_lds0 : (lds_u16*)k_lds1; };
+  auto vslot = [&](int s) { return s == 0 ? (lds_u16*)v_lds0 : (lds_u16*)v_lds1; };
+  // load n of a full tile, or (redirect) the same load into the sink
+  auto load_fast = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, lds_u16* dst, bool is_k, int n, bool redirect) {
+    const int part = (n * RPL) / PART;
+    const int r0 = n * RPL - part * PART;
+    const uint32_t so = ((uint32_t)si.key0[part] + (uint32_t)r0) * RB;
+    lds_u16* d = redirect ? (lds_u16*)sink_lds : dst + n * 64 * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)d, 16,
+                                             (int)chunk_off(n, is_k), (int)so, 0, 0);
+  };
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, lds_u16* dst, bool is_k, int n, bool full) {
+    const int part = (n * RPL) / PART;
+    const int r0 = n * RPL - part * PART;   // first row of the round inside its part
+    const uint32_t so = ((uint32_t)si.key0[part] + (uint32_t)r0) * RB;
+    const uint32_t co = chunk_off(n, is_k);
+    if constexpr (kDma) {
+      const uint32_t vo = full ? co : (vrow < si.valid[part] - r0 ? co + so : kOob);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + n * 64 * 8), 16, (int)vo, (int)(full ? so : 0u), 0, 0);
+    } else {
+      const uint32_t vo = vrow < si.valid[part] - r0 ? co + so : kOob;
+      const uint4 x = Row8<T>::buf(rsrc, vo, 0);
+      *reinterpret_cast<lds_u32x4*>(dst + (n * 64 + lane) * 8) = u32x4{x.x, x.y, x.z, x.w};
     }
-    if constexpr (!kDma) {
+  };
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, lds_u16* dst, bool is_k, auto known_full) {
+    const bool full = decltype(known_full)::value || is_full(si);
 #pragma unroll
-      for (int n = 0; n < NLD; ++n) {
-        *reinterpret_cast<uint4*>(kbuf(b) + (n * NTH + tid) * 8) = kst[n];
-        *reinterpret_cast<uint4*>(vbuf(b) + (n * NTH + tid) * 8) = vst[n];
+    for (int n = 0; n < NLD; ++n) load_one(rsrc, si, dst, is_k, n, full);
+  };
+
+  // ---- S^T(u) = K(u) Q^T ----
+  // K A-operand read of chunk c: tile row qc, logical chunk 2c + hf:
+  // byte address ka ^ (c * 32).
+  const uint32_t ka = (uint32_t)(qc * KCH * 16) | (uint32_t)((hf ^ swz_k(qc)) * 16);
+  auto qk = [&](int ks, f32x16 (&s)[QT]) {
+    const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(ks));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) s[qt] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const bf16x8 kf = lds_frag(kt + (ka ^ (uint32_t)(c * 32)));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qt][c], s[qt], 0, 0, 0);
+    }
+  };
+
+  // accumulator register r of this lane is tile row 8*(r/4) + 4*hf + r%4
+  auto mask = [&](f32x16 (&s)[QT], const Info& si) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int p = row / PART;
+      // (select, not an indexed read: the geometry must stay in scalar registers)
+      const int v = p == 0 ? si.valid[0] : si.valid[NBLK - 1];
+      const bool bad = row - p * PART >= v;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        if (bad) s[qt][r] = -INFINITY;
+    }
+  };
+
+  // row max of S(u) in the log2 domain: the lane's 16 keys, then lane ^ 32
+  auto rowmax = [&](const f32x16 (&s)[QT], const Info& si, float (&mx)[QT]) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const f32x16& x = s[qt];
+      const float m0 = fmaxf(fmaxf(fmaxf(fmaxf(x[0], x[1]), x[2]), fmaxf(x[3], x[4])), fmaxf(fmaxf(x[5], x[6]), x[7]));
+      const float m1 = fmaxf(fmaxf(fmaxf(fmaxf(x[8], x[9]), x[10]), fmaxf(x[11], x[12])),
+                             fmaxf(fmaxf(x[13], x[14]), x[15]));
+      float m;
+      if constexpr (NBLK == 2) m = fmaxf(m0 * a.scale_log2 + si.bias[0], m1 * a.scale_log2 + si.bias[1]);
+      else m = fmaxf(m0, m1) * a.scale_log2 + si.bias[0];
+      mx[qt] = max_xor32(m);
+    }
+  };
+
+  float m_run[QT], l_run[QT];
+  f32x16 o[QT][DT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
+  }
+
+  // lazy rescale: the reference max moves only when a row max grows by more
+  // than kTau (so every p <= 2^kTau); O and l are rescaled only then
+  auto rescale = [&](const float (&mx)[QT]) {
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > m_run[qt] + kTau;
+    if (__any(grow)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float m_new = mx[qt] > m_run[qt] + kTau ? mx[qt] : m_run[qt];
+        const float alpha = fast_exp2(m_run[qt] - (m_new == -INFINITY ? 0.0f : m_new));
+        m_run[qt] = m_new;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          o[qt][dt] *= alpha;
+          // one tile at a time: each is back in its accumulators before the next
+          if constexpr (kDma) asm volatile("" : "+a"(o[qt][dt]));
+        }
       }
     }
   };
 
-  // ---- one sub-tile: S^T = K Q^T, online softmax, O^T += V^T P^T ----
-  // accumulator register r of this lane is tile row 8*(r/4) + 4*hf + r%4
-  auto compute = [&](const SubInfo& si, int b) {
-    const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbuf(b));
-    const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbuf(b));
-    f32x16 sc = f32x16{};
-    {
-      bf16x8 kf[KC];
+  // P(u) = exp2(S(u) * scale + bias - m) as bf16 P^T B operands; the row sum
+  // adds exactly these bf16 values (v_dot2 with ones).  P^T B operand of key
+  // chunk c holds keys 16c + 8(e/4) + 4hf + e%4 = accumulator registers 8c + e.
+  auto softmax = [&](const f32x16 (&s)[QT], const Info& si, bf16x8 (&pb)[QT][2]) {
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kf[c] = as_frag(*reinterpret_cast<const uint4*>(kt + (ka ^ (uint32_t)(c * 32))));
-#pragma unroll
-      for (int c = 0; c < KC; ++c) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], sc, 0, 0, 0);
-    }
-    bool full = true;
-#pragma unroll
-    for (int p = 0; p < NBLK; ++p) full = full && si.valid[p] == PART;
-    if (!full) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
-        const int p = row / PART;
-        if (row - p * PART >= si.valid[p]) sc[r] = -INFINITY;
-      }
-    }
-    // row max: the lane's 16 keys (v_max3 chains), then lane ^ 32 (scale > 0,
-    // one weight per part)
-    const float mx0 = fmaxf(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), sc[2]), fmaxf(sc[3], sc[4])),
-                            fmaxf(fmaxf(sc[5], sc[6]), sc[7]));
-    const float mx1 = fmaxf(fmaxf(fmaxf(fmaxf(sc[8], sc[9]), sc[10]), fmaxf(sc[11], sc[12])),
-                            fmaxf(fmaxf(sc[13], sc[14]), sc[15]));
-    float mx;
-    if constexpr (NBLK == 2) mx = fmaxf(mx0 * a.scale_log2 + si.bias[0], mx1 * a.scale_log2 + si.bias[1]);
-    else mx = fmaxf(mx0, mx1) * a.scale_log2 + si.bias[0];
-    mx = max_xor32(mx);
-    // lazy rescale: the reference max moves only when the row max grows by more
-    // than kTau (so p <= 2^kTau); O and l are rescaled only then
-    if (__any(mx > m_run + kTau)) {
-      const float m_new = mx > m_run + kTau ? mx : m_run;
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    const float mu = m_run == -INFINITY ? 0.0f : m_run;
-    const float off0 = si.bias[0] - mu;
-    const float off1 = si.bias[NBLK - 1] - mu;
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r] * a.scale_log2 + (r < 8 ? off0 : off1));
-    // P^T B operand of key chunk c: keys 16c + 8(e/4) + 4hf + e%4 = registers 8c + e;
-    // the row sum adds exactly these bf16 values (v_dot2 with ones)
-    bf16x8 pb[2];
-    float ps = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        w[k2] = pack_bf16x2(p[8 * c + 2 * k2], p[8 * c + 2 * k2 + 1]);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k2]), kOnes2, ps, false);
-      }
-      pb[c] = as_frag(make_uint4(w[0], w[1], w[2], w[3]));
-    }
-    l_run += ps;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      bf16x8 vf[2];
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
+      const float off0 = si.bias[0] - mu;
+      const float off1 = si.bias[NBLK - 1] - mu;
+      float ps = 0.0f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const unsigned char* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
+        uint32_t w[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int r = 8 * c + 2 * k2;
+          const float p0 = fast_exp2(s[qt][r] * a.scale_log2 + (r < 8 ? off0 : off1));
+          const float p1 = fast_exp2(s[qt][r + 1] * a.scale_log2 + (r < 8 ? off0 : off1));
+          w[k2] = pack_bf16x2(p0, p1);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k2]), kOnes2, ps, false);
+        }
+        pb[qt][c] = as_frag(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      l_run[qt] += ps;
+    }
+  };
+
+  // V^T A-operand transposing reads: 16-lane group g = lane/16 covers d columns
+  // 16*(g & 1) + [0, 16) of d tile dt; lane i of the group addresses tile row
+  // 16c + 8hh + 4hf + i/4 and columns 32dt + 16(g & 1) + 4(i & 3):
+  // byte address va ^ (dt * 64) + (16c + 8hh) rows.
+  const uint32_t va = [&] {
+    const int i = lane & 15, g = lane >> 4;
+    const int r = 4 * hf + (i >> 2);
+    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
+    return (uint32_t)(r * D * 2) | (uint32_t)((lc ^ swz_v<D>(r)) * 16) | (uint32_t)((i & 1) * 8);
+  }();
+  auto pv = [&](int vs, const bf16x8 (&pb)[QT][2]) {
+    const lds_u8* vt = reinterpret_cast<const lds_u8*>(vslot(vs));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const lds_u8* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
         const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
         const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
-        vf[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int c = 0; c < 2; ++c) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], pb[c], o[dt], 0, 0, 0);
+        for (int qt = 0; qt < QT; ++qt) o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qt][c], o[qt][dt], 0, 0, 0);
+      }
     }
   };
 
-  // ---- pipeline: one barrier per sub-tile ----
-  // step u: wait for this wave's loads of sub-tile u, barrier (everyone's data
-  // of u is in buffer u&1 and buffer (u+1)&1 is no longer read), start loading
-  // sub-tile u+1 into buffer (u+1)&1, compute sub-tile u.
-  SubInfo si_cur;
-  Raw raw_next;
+  // Hazard fences for vector code that reads MFMA results: the nops, then
+  // empty ordering points on the values, so the reads cannot move above them.
+  auto fence_s = [&](f32x16 (&t)[QT]) {
+    asm volatile("s_nop 11" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(t[qt]));
+  };
+  auto fence_o = [&]() {
+    asm volatile("s_nop 11" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[qt][dt]));
+  };
+
+  // ---- pipeline ----
+  // Step u (p = u & 1): sc[p] holds S(u) (masked, its max folded into
+  // m_run); K(u+1) is in K slot (u+1) % 2 and V(u) in V slot u % 2.
+  //   phase 1: S(u+1) MFMAs into sc[p^1], each followed by a pair of
+  //            exponentials of S(u) (P(u) and its row sums); V(u+1) loads into
+  //            V slot (u+1) % 2 (last read by step u-1) between them;
+  //   phase 2: P(u) V(u) MFMAs, with K(u+3) loads into K slot (u+1) % 2 (read
+  //            in phase 1) between them; the mask and row max of S(u+1) run
+  //            after the third of them;
+  //   then the rescale for S(u+1) if a row max grew past the tolerance.
+  // Sub-tiles past the list load zeros and never reach O.  The waits for the
+  // tile loads are derived by the compiler from the LDS slot each read touches.
   if (nsub > 0) {
-    si_cur = make_info(0, fetch(0));
-    load_tiles(si_cur, 0);
-    if (nsub > 1) raw_next = fetch(1);
-  }
-  for (int u = 0; u < nsub; ++u) {
-    const int b = u & 1;
-    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    SubInfo si_next;
-    if (u + 1 < nsub) {
-      si_next = make_info(u + 1, raw_next);
-      load_tiles(si_next, b ^ 1);
-      if (u + 2 < nsub) raw_next = fetch(u + 2);
+    f32x16 sc[2][QT];
+    Info i_u = info(0, fetch(0));   // sub-tile u
+    Info i_u1 = info(1, fetch(1));  // u + 1
+    Info i_u2 = info(2, fetch(2));  // u + 2
+    Raw r3 = fetch(3);              // u + 3
+    load_tile(rk, i_u, kslot(0), true, std::false_type{});
+    load_tile(rk, i_u1, kslot(1), true, std::false_type{});
+    load_tile(rv, i_u, vslot(0), false, std::false_type{});
+    if constexpr (kDma) {
+      // S(0) (the Q fragments were just written into AGPRs by vector moves)
+      asm volatile("s_nop 1" ::: "memory");
+      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(0));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8 kf = lds_frag(kt + (ka ^ (uint32_t)(c * 32)));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          if (c == 0) mma_s_first(sc[0][qt], kf, qf[qt][c]);
+          else mma_s(sc[0][qt], kf, qf[qt][c]);
+        }
+      }
+      load_tile(rk, i_u2, kslot(0), true, std::false_type{});
+      fence_s(sc[0]);
+    } else {
+      qk(0, sc[0]);
+      load_tile(rk, i_u2, kslot(0), true, std::false_type{});
     }
-    compute(si_cur, b);
-    si_cur = si_next;
+    if (!is_full(i_u)) mask(sc[0], i_u);
+    {
+      float mx[QT];
+      rowmax(sc[0], i_u, mx);
+      rescale(mx);
+    }
+
+    // one step of the matrix-core pipeline (bf16 tiles in LDS by DMA)
+    auto step_mma = [&](auto par, int u, const Info& i_u3, Raw& r4) {
+      constexpr int p = decltype(par)::value;   // u & 1
+      f32x16 (&scur)[QT] = sc[p];
+      f32x16 (&snext)[QT] = sc[p ^ 1];
+      const bool part_v = !is_full(i_u1);    // V(u+1) / S(u+1) has invalid keys
+      const bool part_k = !is_full(i_u3);    // K(u+3) has invalid keys
+      // softmax offsets of S(u): bias of each part minus the reference max
+      float off[QT][NBLK];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) off[qt][b] = i_u.bias[b] - m_run[qt];
+      // a partial V(u+1) is loaded here with zeroed rows; the interleaved
+      // loads below then go to the sink
+      if (part_v) load_tile(rv, i_u1, vslot(p ^ 1), false, std::false_type{});
+      // K(u+1) fragments
+      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(p ^ 1));
+      bf16x8 kf[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kf[c] = lds_frag(kt + (ka ^ (uint32_t)(c * 32)));
+      // ---- phase 1 ----
+      constexpr int NM = KC * QT;          // MFMAs of S(u+1)
+      constexpr int NPAIR = QT * 8;        // exponential pairs of S(u)
+      constexpr int PPM = NPAIR / NM;      // pairs after each MFMA
+      uint32_t pw[QT][8];
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int c = i / QT, qt2 = i % QT;
+        if (i > 0) {
+          // the pairs issued after MFMA i-1 are complete before MFMA i
+#pragma unroll
+          for (int e = 0; e < PPM; ++e) {
+            const int pi = (i - 1) * PPM + e;
+            pin_before(pw[pi / 8][pi % 8]);
+            pin_before(l_run[pi / 8]);
+          }
+        }
+        if (c == 0) mma_s_first(snext[qt2], kf[c], qf[qt2][c]);
+        else mma_s(snext[qt2], kf[c], qf[qt2][c]);
+        if (i < NLD) load_fast(rv, i_u1, vslot(p ^ 1), false, i, part_v);
+#pragma unroll
+        for (int e = 0; e < PPM; ++e) {
+          const int pi = i * PPM + e;
+          const int qt = pi / 8, k = pi % 8;
+          const int b = (2 * k < 8) ? 0 : NBLK - 1;
+          pin_after(off[qt][b]);
+          const float p0 = fast_exp2(scur[qt][2 * k] * a.scale_log2 + off[qt][b]);
+          const float p1 = fast_exp2(scur[qt][2 * k + 1] * a.scale_log2 + off[qt][b]);
+          pw[qt][k] = pack_bf16x2(p0, p1);
+          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[qt][k]), kOnes2, l_run[qt], false);
+        }
+      }
+      bf16x8 pb[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          pb[qt][c] = as_frag(make_uint4(pw[qt][4 * c], pw[qt][4 * c + 1], pw[qt][4 * c + 2], pw[qt][4 * c + 3]));
+      if (part_v) {
+        fence_s(snext);
+        mask(snext, i_u1);
+      }
+      // a partial K(u+3) goes into K slot (u+1) % 2 now that phase 1 has read it
+      if (part_k) load_tile(rk, i_u3, kslot(p ^ 1), true, std::false_type{});
+      // ---- phase 2 ----
+      // V(u) fragment f+1 is read before the MFMAs of fragment f.
+      const lds_u8* vt = reinterpret_cast<const lds_u8*>(vslot(p));
+      constexpr int NVF = DT * 2;          // V fragments
+      auto read_vf = [&](int f) {
+        const int dt = f / 2, c = f % 2;
+        const auto* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
+        const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
+        const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vf_cur = read_vf(0);
+#pragma unroll
+      for (int f = 0; f < NVF; ++f) {
+        const int dt = f / 2, c = f % 2;
+        bf16x8 vf_nxt;
+        if (f + 1 < NVF) vf_nxt = read_vf(f + 1);
+        if (f + 1 == NVF) r4 = fetch(u + 4);   // list entries of u+4, after the last LDS read
+        if (f == 0) {
+          // the last exponential pairs are complete, and 2 wait states separate
+          // their P writes from the first MFMA that reads them
+#pragma unroll
+          for (int e = 0; e < PPM; ++e) {
+            const int pi = (NM - 1) * PPM + e;
+            pin_before(pw[pi / 8][pi % 8]);
+            pin_before(l_run[pi / 8]);
+          }
+          asm volatile("s_nop 1" ::: "memory");
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int j = f * QT + qt;
+          mma_o(o[qt][dt], vf_cur, pb[qt][c]);
+          if (j < NLD) load_fast(rk, i_u3, kslot(p ^ 1), true, j, part_k);
+          if (j == 2) {
+            // the row max of S(u+1) starts here, 12+ wait states after its last MFMA
+            asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < QT; ++t) asm volatile("" : "+v"(snext[t]));
+          }
+        }
+        vf_cur = vf_nxt;
+      }
+    };
+
+    auto step = [&](auto par, auto full, int u, const Info& i_u3) {
+      constexpr int p = decltype(par)::value;   // u & 1
+      constexpr bool kFull = decltype(full)::value;
+      Raw r4;
+      if constexpr (kDma) {
+        step_mma(par, u, i_u3, r4);
+      } else {
+        r4 = fetch(u + 4);
+        load_tile(rv, i_u1, vslot(p ^ 1), false, full);
+        bf16x8 pb[QT][2];
+        qk(p ^ 1, sc[p ^ 1]);
+        softmax(sc[p], i_u, pb);
+        if constexpr (!kFull) {
+          if (!is_full(i_u1)) mask(sc[p ^ 1], i_u1);
+        }
+        pv(p, pb);
+        load_tile(rk, i_u3, kslot(p ^ 1), true, full);
+      }
+      float mx[QT];
+      rowmax(sc[p ^ 1], i_u1, mx);
+      if (u + 1 < nsub) {
+        if constexpr (kDma) {
+          // vector reads of O (rescale) 12+ wait states after the last P V MFMA
+          bool grow = false;
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > m_run[qt] + kTau;
+          if (__any(grow)) {
+            fence_o();
+            rescale(mx);
+          }
+        } else {
+          rescale(mx);
+        }
+      }
+      i_u = i_u1;
+      i_u1 = i_u2;
+      i_u2 = info(u + 3, r3);
+      r3 = r4;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto step_any = [&](auto par, int u) {
+      const Info i_u3 = info(u + 3, r3);
+      if constexpr (kDma) {
+        step(par, std::true_type{}, u, i_u3);   // partial tiles are handled inside
+      } else {
+        if (is_full(i_u1) && is_full(i_u3)) step(par, std::true_type{}, u, i_u3);
+        else step(par, std::false_type{}, u, i_u3);
+      }
+    };
+    for (int u = 0; u < nsub; u += 2) {
+      step_any(I0{}, u);
+      if (u + 1 < nsub) step_any(I1{}, u + 1);
+    }
   }
-  __syncthreads();
+  // vector reads of O (epilogue) 12+ wait states after the last P V MFMA
+  if constexpr (kDma) fence_o();
+  // the last sub-tiles' (zero) loads must land before the LDS is reused
+  if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
-  const float l = add_xor32(l_run);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  float* ostage = reinterpret_cast<float*>(tiles) + wave * 32 * OS;
-  // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<f32x4*>(ostage + qc * OS + 32 * dt + 8 * r4 + 4 * hf) =
-          f32x4{o[dt][4 * r4], o[dt][4 * r4 + 1], o[dt][4 * r4 + 2], o[dt][4 * r4 + 3]} * inv;
-  if (hf == 0 && a.lse) {
-    const int64_t row = q0 + qc;
-    const float mu = m_run == -INFINITY ? 0.0f : m_run;
-    if (row < a.seq_alloc)
-      a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
+  // 16 rows of float32 per pass in K slot 0, 16-byte chunks XOR-swizzled by
+  // the row so the column writes of 16 rows fall on distinct banks.
+  float* ostage = reinterpret_cast<float*>(k_lds0);
   T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
   constexpr int C8 = D / 8;
-  for (int e = lane; e < 32 * C8; e += 64) {
-    const int q = e / C8, c8 = e % C8;
-    const int64_t row = q0 + q;
-    if (row >= a.seq_alloc) continue;
-    float v[8];
-    if (row < a.S) {
-      const float4 x = *reinterpret_cast<const float4*>(ostage + q * OS + c8 * 8);
-      const float4 y = *reinterpret_cast<const float4*>(ostage + q * OS + c8 * 8 + 4);
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-      v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-    } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l = add_xor32(l_run[qt]);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int64_t qrow0 = q0 + 32 * qt;
+    if (hf == 0 && a.lse) {
+      const int64_t row = qrow0 + qc;
+      const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
+      if (row < a.seq_alloc)
+        a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
     }
-    store8<T>(Ob + row * D + c8 * 8, v);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
+      if ((qc >> 4) == half) {
+        const int q = qc & 15;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x16 t = o[qt][dt];
+          if constexpr (kDma) asm volatile("" : "+v"(t));   // one tile in vector registers at a time
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int ch = 8 * dt + 2 * r4 + hf;
+            *reinterpret_cast<f32x4*>(ostage + q * D + ((ch ^ q) * 4)) =
+                f32x4{t[4 * r4], t[4 * r4 + 1], t[4 * r4 + 2], t[4 * r4 + 3]} * inv;
+          }
+        }
+      }
+      for (int e = lane; e < 16 * C8; e += 64) {
+        const int q = e / C8, c8 = e % C8;
+        const int64_t row = qrow0 + 16 * half + q;
+        if (row >= a.seq_alloc) continue;
+        float v[8];
+        if (row < a.S) {
+          const float4 x = *reinterpret_cast<const float4*>(ostage + q * D + (((2 * c8) ^ q) * 4));
+          const float4 y = *reinterpret_cast<const float4*>(ostage + q * D + (((2 * c8 + 1) ^ q) * 4));
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+          v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+        }
+        store8<T>(Ob + row * D + c8 * 8, v);
+      }
+    }
   }
 }
 
-template <typename T, int D, int QROWS>
+template <typename T, int D, int QT>
 hipError_t launch_bk(const FwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)forward_grid(a));
-  const dim3 block(QROWS * 2);
+  const dim3 block(64);
   switch (a.k_block) {
-    case 16: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 16>), grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 32>), grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((fwd_kernel<T, D, QROWS, 64>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((fwd_kernel<T, D, QT, 16>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((fwd_kernel<T, D, QT, 32>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((fwd_kernel<T, D, QT, 64>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -533,7 +799,7 @@ hipError_t launch_bk(const FwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_q(const FwdArgs& a, hipStream_t stream) {
-  return a.q_block == 32 ? launch_bk<T, D, 32>(a, stream) : launch_bk<T, D, 64>(a, stream);
+  return a.q_block == 32 ? launch_bk<T, D, 1>(a, stream) : launch_bk<T, D, 2>(a, stream);
 }
 
 template <typename T>
