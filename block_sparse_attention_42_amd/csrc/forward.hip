@@ -123,21 +123,27 @@ __device__ __forceinline__ float add_xor32(float x) {
 
 // ---- matrix instructions with fixed register files ----
 // The score tiles S^T are produced by MFMAs and consumed by vector code, so
-// they live in VGPRs; the O^T accumulators and the Q fragments are only ever
-// MFMA operands and live in AGPRs.  The compiler cannot be told that per
+// they live in VGPRs; the O^T accumulators, the Q fragments and the K and V
+// fragments read from LDS are only ever MFMA operands and live in AGPRs.  The compiler cannot be told that per
 // instruction, so these MFMAs are written as inline assembly with register
 // class constraints.  Because the compiler does not see them as MFMAs, the
 // code around them keeps the hardware's wait-state rules itself: a vector
 // write of an MFMA source needs 2 wait states before the MFMA, and a vector
 // read of an MFMA result needs 12 after it (8-pass 32x32x16).
 __device__ __forceinline__ void mma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b) : "memory");
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "a"(a), "a"(b) : "memory");
 }
 __device__ __forceinline__ void mma_s(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b) : "memory");
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "a"(a), "a"(b) : "memory");
 }
 __device__ __forceinline__ void mma_o(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b) : "memory");
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "a"(a), "v"(b) : "memory");
+}
+// max of three floats (no NaN canonicalization: the inputs are finite or -inf)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 // The "memory" clobber keeps every memory instruction (tile loads, LDS reads)
 // where the source puts it relative to these MFMAs.
@@ -207,7 +213,6 @@ void fwd_kernel(FwdArgs a) {
   constexpr int NBLK = BK >= SUB ? 1 : SUB / BK;   // key blocks per sub-tile
   constexpr int PART = SUB / NBLK;
   constexpr float kTau = 8.0f;         // lazy rescale: tolerated growth of the running max (log2)
-  constexpr int LOPS = NLD * (kDma ? 1 : Row8<T>::kOps);   // VMEM instructions per tile
   static_assert(NBLK <= 2 && PART % RPL == 0 && NLD >= 1, "tile shape");
   // One LDS array per ring slot: the compiler then knows which tile loads a
   // read can depend on, and never waits for the loads still in flight into
@@ -216,7 +221,8 @@ void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_E], v_lds1[TILE_E];
   // destination of the tile loads of a step whose tile is loaded separately
   // (partial tiles): the instructions still run, their data is discarded
-  __shared__ __attribute__((aligned(16))) uint16_t sink_lds[64 * 8];
+  // (4 KB: a group of loads writes up to 4 consecutive KB)
+  __shared__ __attribute__((aligned(16))) uint16_t sink_lds[4 * 64 * 8];
 
   const int lane = threadIdx.x;
   const int qc = lane & 31;            // query column of S^T / O^T, key row of the K operand
@@ -235,12 +241,7 @@ void fwd_kernel(FwdArgs a) {
   const int64_t q0 = (int64_t)qb * a.q_block;
   const int S32 = (int)a.S;
 
-  // List entries are read-only for the whole launch: read them through the
-  // constant address space, so uniform indices become scalar loads.
-  typedef const __attribute__((address_space(4))) int32_t* cint_p;
-  typedef const __attribute__((address_space(4))) float* cflt_p;
-  const cint_p lst = (cint_p)(a.idx + rowid * a.nkb);
-  const cflt_p lwr = a.logw ? (cflt_p)(a.logw + rowid * a.nkb) : nullptr;
+  const bool has_w = a.logw != nullptr;
 
   const uint32_t nbytes = (uint32_t)a.seq_alloc * RB;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Qb, 0, (int)nbytes, 0x00020000);
@@ -265,9 +266,18 @@ void fwd_kernel(FwdArgs a) {
     for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(qf[qt][c]));
 
   // ---- sub-tile geometry: first key, valid keys and log2 weight of each part ----
+  // The list entries (and log-weights) of a sub-tile are fetched by vector
+  // loads, lane b taking part b, several steps before they are needed: the
+  // loads are ordered with the tile loads, so no wait on them ever blocks the
+  // LDS reads (as a scalar-cache load's wait would).
+  const uint32_t lbytes = (uint32_t)a.nkb * 4u;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + rowid * a.nkb), 0, (int)lbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(has_w ? (void*)(a.logw + rowid * a.nkb) : (void*)(a.idx + rowid * a.nkb), 0,
+                                        (int)lbytes, 0x00020000);
   struct Raw {
-    int j[NBLK];
-    float w[NBLK];
+    int j;      // lane b: list entry of part b
+    int w;      // lane b: its log-weight bits
   };
   struct Info {
     int key0[NBLK];      // first key of each part (0 if none)
@@ -275,16 +285,12 @@ void fwd_kernel(FwdArgs a) {
     float bias[NBLK];    // log2-domain weight of each part
   };
   auto fetch = [&](int u) {
+    const int b = lane < NBLK ? lane : 0;
+    const int pos = (u * SUB + b * PART) / BK;
+    const uint32_t off = (uint32_t)min(pos, max(cnt - 1, 0)) * 4u;   // every row has nkb >= 1 slots
     Raw r;
-#pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
-      const int pos = (u * SUB + b * PART) / BK;
-      const int pc = min(pos, max(cnt - 1, 0));   // every row has nkb >= 1 slots
-      const int j = lst[pc];
-      r.j[b] = __builtin_amdgcn_readfirstlane((pos < cnt && j >= 0 && j < a.nkb) ? j : -1);
-      r.w[b] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                   __builtin_bit_cast(int, (pos < cnt && lwr) ? lwr[pc] : 0.0f)));
-    }
+    r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)off, 0, 0);
+    r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
     return r;
   };
   auto info = [&](int u, const Raw& r) {
@@ -292,11 +298,14 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int g = u * SUB + b * PART;
-      const int j = r.j[b];
+      const int pos = g / BK;
+      const int jr = __builtin_amdgcn_readlane(r.j, b);
+      const int j = (pos < cnt && jr >= 0 && jr < a.nkb) ? jr : -1;
       const int key0 = j * BK + g % BK;
       si.key0[b] = j >= 0 ? key0 : 0;
       si.valid[b] = j >= 0 ? min(max(S32 - key0, 0), PART) : 0;
-      si.bias[b] = j >= 0 ? r.w[b] * 1.4426950408889634f : 0.0f;
+      const float w = has_w ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(r.w, b)) : 0.0f;
+      si.bias[b] = j >= 0 ? w * 1.4426950408889634f : 0.0f;
     }
     return si;
   };
@@ -334,14 +343,26 @@ void fwd_kernel(FwdArgs a) {
   };
   auto kslot = [&](int s) { return s == 0 ? (lds_u16*)k_lds0 : (lds_u16*)k_lds1; };
   auto vslot = [&](int s) { return s == 0 ? (lds_u16*)v_lds0 : (lds_u16*)v_lds1; };
-  // load n of a full tile, or (redirect) the same load into the sink
+  // load n of a full tile, or (redirect) the same load into the sink.  The
+  // instruction's immediate offset moves both the global and the LDS address,
+  // so the loads of one group of G rounds share one scalar offset and one LDS
+  // base (M0) and differ only in the immediate (n % G) KB; a group never
+  // straddles two key blocks.
+  constexpr int G = (PART / RPL) < 4 ? (PART / RPL) : 4;
   auto load_fast = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, lds_u16* dst, bool is_k, int n, bool redirect) {
-    const int part = (n * RPL) / PART;
-    const int r0 = n * RPL - part * PART;
+    const int g0 = (n / G) * G;                 // first round of the group
+    const int part = (g0 * RPL) / PART;
+    const int r0 = g0 * RPL - part * PART;
     const uint32_t so = ((uint32_t)si.key0[part] + (uint32_t)r0) * RB;
-    lds_u16* d = redirect ? (lds_u16*)sink_lds : dst + n * 64 * 8;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)d, 16,
-                                             (int)chunk_off(n, is_k), (int)so, 0, 0);
+    lds_u16* d = redirect ? (lds_u16*)sink_lds : dst + g0 * 64 * 8;
+    auto* ld = (__attribute__((address_space(3))) void*)d;
+    const int vo = (int)chunk_off(n, is_k);
+    switch (n % G) {   // the immediate must be a literal; n is known after unrolling
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 1024, 0); break;
+      case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 2048, 0); break;
+      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 3072, 0); break;
+    }
   };
   auto load_one = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, lds_u16* dst, bool is_k, int n, bool full) {
     const int part = (n * RPL) / PART;
@@ -512,6 +533,18 @@ void fwd_kernel(FwdArgs a) {
       for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[qt][dt]));
   };
 
+  // Vector-memory instructions retire in issue order, and every step issues
+  // them in the same order: its two list loads, the NLD V(u+1) loads (phase
+  // 1), the NLD K(u+3) loads (phase 2); a partial tile adds its own NLD loads
+  // before them.  When the V(u) fragments are read (late in phase 1) and when
+  // the K(u+2) fragments are read (late in phase 2), the tile they need was
+  // followed by at least 2 + 2 NLD other loads, so waiting until at most that
+  // many are outstanding is enough (and merely conservative after a partial
+  // tile).  In the prologue a tile is followed by two others (2 NLD loads).
+  auto tile_wait = [&]() {
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 + 2 * NLD) : "memory");
+  };
+
   // ---- pipeline ----
   // Step u (p = u & 1): sc[p] holds S(u) (masked, its max folded into
   // m_run); K(u+1) is in K slot (u+1) % 2 and V(u) in V slot u % 2.
@@ -530,12 +563,14 @@ void fwd_kernel(FwdArgs a) {
     Info i_u1 = info(1, fetch(1));  // u + 1
     Info i_u2 = info(2, fetch(2));  // u + 2
     Raw r3 = fetch(3);              // u + 3
+    Raw r4 = fetch(4);              // u + 4
     load_tile(rk, i_u, kslot(0), true, std::false_type{});
     load_tile(rk, i_u1, kslot(1), true, std::false_type{});
     load_tile(rv, i_u, vslot(0), false, std::false_type{});
     if constexpr (kDma) {
-      // S(0) (the Q fragments were just written into AGPRs by vector moves)
-      asm volatile("s_nop 1" ::: "memory");
+      // S(0) (the Q fragments were just written into AGPRs by vector moves);
+      // K(0) was followed by the K(1) and V(0) loads
+      asm volatile("s_waitcnt vmcnt(%0)\n s_nop 1" ::"n"(2 * NLD) : "memory");
       const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(0));
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
@@ -559,8 +594,25 @@ void fwd_kernel(FwdArgs a) {
       rescale(mx);
     }
 
+    bf16x8 kf[KC];          // K(u+1) fragments at the start of step u
+    float row_mx[QT];       // row max of S(u+1), in the log2 domain
+    if constexpr (kDma) {
+      // K(1) was followed by the V(0) and K(2) loads
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NLD) : "memory");
+      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(1));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kf[c] = lds_frag(kt + (ka ^ (uint32_t)(c * 32)));
+    }
     // one step of the matrix-core pipeline (bf16 tiles in LDS by DMA)
-    auto step_mma = [&](auto par, int u, const Info& i_u3, Raw& r4) {
+    //   phase 1: the S(u+1) MFMAs (K(u+1) fragments read at the end of the
+    //            previous step), with the exponentials of the first half of the
+    //            keys of S(u) and the V(u+1) loads between them;
+    //   phase 2: the P(u) V(u) MFMAs, first half of the keys first: the
+    //            exponentials of the second half run between the first half's
+    //            MFMAs, the row max of S(u+1) between the second half's; the
+    //            K(u+3) loads go in between, V fragments are read two ahead,
+    //            and the K(u+2) fragments for the next step are read last.
+    auto step_mma = [&](auto par, int u, const Info& i_u3) {
       constexpr int p = decltype(par)::value;   // u & 1
       f32x16 (&scur)[QT] = sc[p];
       f32x16 (&snext)[QT] = sc[p ^ 1];
@@ -575,109 +627,161 @@ void fwd_kernel(FwdArgs a) {
       // a partial V(u+1) is loaded here with zeroed rows; the interleaved
       // loads below then go to the sink
       if (part_v) load_tile(rv, i_u1, vslot(p ^ 1), false, std::false_type{});
-      // K(u+1) fragments
-      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(p ^ 1));
-      bf16x8 kf[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) kf[c] = lds_frag(kt + (ka ^ (uint32_t)(c * 32)));
-      // ---- phase 1 ----
-      constexpr int NM = KC * QT;          // MFMAs of S(u+1)
-      constexpr int NPAIR = QT * 8;        // exponential pairs of S(u)
-      constexpr int PPM = NPAIR / NM;      // pairs after each MFMA
+
+      // exponential pair k (keys 2k, 2k+1 of the lane's half) of q-tile qt
       uint32_t pw[QT][8];
+      // exponential pair k (keys 2k, 2k+1 of the lane's half) of every q-tile:
+      // the q-tiles' chains are independent, so their latencies overlap
+      auto pair = [&](int k) {
+        const int b = (2 * k < 8) ? 0 : NBLK - 1;
+        float p0[QT], p1[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) pin_after(off[qt][b]);   // after the MFMA before it
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          p0[qt] = scur[qt][2 * k] * a.scale_log2 + off[qt][b];
+          p1[qt] = scur[qt][2 * k + 1] * a.scale_log2 + off[qt][b];
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          p0[qt] = fast_exp2(p0[qt]);
+          p1[qt] = fast_exp2(p1[qt]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) pw[qt][k] = pack_bf16x2(p0[qt], p1[qt]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[qt][k]), kOnes2, l_run[qt], false);
+          pin_before(pw[qt][k]);               // before the MFMA after it
+          pin_before(l_run[qt]);
+        }
+      };
+
+      const lds_u8* vt = reinterpret_cast<const lds_u8*>(vslot(p));
+      constexpr int NVF = DT * 2;          // V fragments, c-major: f = c * DT + dt
+      auto read_vf = [&](int f) {
+        const int c = f / DT, dt = f % DT;
+        const lds_u8* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
+        const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
+        const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vfr[NVF];
+      // ---- phase 1: pairs k = 0..3 of each q-tile (P chunk c = 0) ----
+      constexpr int NM = KC * QT;          // MFMAs of S(u+1)
+      constexpr int NP1 = 4;               // pair groups in phase 1 (k = 0..3)
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         const int c = i / QT, qt2 = i % QT;
-        if (i > 0) {
-          // the pairs issued after MFMA i-1 are complete before MFMA i
-#pragma unroll
-          for (int e = 0; e < PPM; ++e) {
-            const int pi = (i - 1) * PPM + e;
-            pin_before(pw[pi / 8][pi % 8]);
-            pin_before(l_run[pi / 8]);
-          }
+        // the first two V(u) fragments are read during the last MFMAs of phase 1
+        if (i == NM - 4) {
+          tile_wait();   // V(u) landed
+          vfr[0] = read_vf(0);
+          if (NVF > 1) vfr[1] = read_vf(1);
         }
+        // pairs placed after MFMA i: e with e * NM / NP1 == i
         if (c == 0) mma_s_first(snext[qt2], kf[c], qf[qt2][c]);
         else mma_s(snext[qt2], kf[c], qf[qt2][c]);
         if (i < NLD) load_fast(rv, i_u1, vslot(p ^ 1), false, i, part_v);
 #pragma unroll
-        for (int e = 0; e < PPM; ++e) {
-          const int pi = i * PPM + e;
-          const int qt = pi / 8, k = pi % 8;
-          const int b = (2 * k < 8) ? 0 : NBLK - 1;
-          pin_after(off[qt][b]);
-          const float p0 = fast_exp2(scur[qt][2 * k] * a.scale_log2 + off[qt][b]);
-          const float p1 = fast_exp2(scur[qt][2 * k + 1] * a.scale_log2 + off[qt][b]);
-          pw[qt][k] = pack_bf16x2(p0, p1);
-          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[qt][k]), kOnes2, l_run[qt], false);
+        for (int e = 0; e < NP1; ++e) {
+          if (e * NM / NP1 == i) pair(e);
         }
       }
-      bf16x8 pb[QT][2];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          pb[qt][c] = as_frag(make_uint4(pw[qt][4 * c], pw[qt][4 * c + 1], pw[qt][4 * c + 2], pw[qt][4 * c + 3]));
       if (part_v) {
         fence_s(snext);
         mask(snext, i_u1);
       }
       // a partial K(u+3) goes into K slot (u+1) % 2 now that phase 1 has read it
       if (part_k) load_tile(rk, i_u3, kslot(p ^ 1), true, std::false_type{});
+
       // ---- phase 2 ----
-      // V(u) fragment f+1 is read before the MFMAs of fragment f.
-      const lds_u8* vt = reinterpret_cast<const lds_u8*>(vslot(p));
-      constexpr int NVF = DT * 2;          // V fragments
-      auto read_vf = [&](int f) {
-        const int dt = f / 2, c = f % 2;
-        const auto* vp = vt + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
-        const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
-        const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      bf16x8 pb[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        pb[qt][0] = as_frag(make_uint4(pw[qt][0], pw[qt][1], pw[qt][2], pw[qt][3]));
+      // 2 wait states between the last P writes and the first MFMA reading them
+      asm volatile("s_nop 1" ::: "memory");
+      constexpr int NH = DT * QT;          // MFMAs per half
+      constexpr int NP2 = 4;               // pair groups k = 4..7 in the first half
+      float mx[QT];
+      // row max of S(u+1), in steps spread over the second half
+      float rm[QT][6];
+      auto rowmax_part = [&](int qt, int st) {
+        const f32x16& x = snext[qt];
+        float* r = rm[qt];
+        switch (st) {
+          case 0: r[0] = max3(x[0], x[1], x[2]); r[1] = max3(x[3], x[4], x[5]); pin_before(r[1]); break;
+          case 1: r[2] = max3(x[8], x[9], x[10]); r[3] = max3(x[11], x[12], x[13]); pin_before(r[3]); break;
+          case 2: r[0] = max3(r[0], r[1], x[6]); r[2] = max3(r[2], r[3], x[14]); pin_before(r[2]); break;
+          case 3: {
+            r[0] = fmaxf(r[0], x[7]);
+            r[2] = fmaxf(r[2], x[15]);
+            float m;
+            if constexpr (NBLK == 2) m = fmaxf(r[0] * a.scale_log2 + i_u1.bias[0], r[2] * a.scale_log2 + i_u1.bias[1]);
+            else m = fmaxf(r[0], r[2]) * a.scale_log2 + i_u1.bias[0];
+            r[4] = m;
+            pin_before(r[4]);
+            break;
+          }
+          default: mx[qt] = max_xor32(r[4]); pin_before(mx[qt]); break;
+        }
       };
-      bf16x8 vf_cur = read_vf(0);
+      constexpr int NRS = 5;               // row max steps per q-tile
 #pragma unroll
-      for (int f = 0; f < NVF; ++f) {
-        const int dt = f / 2, c = f % 2;
-        bf16x8 vf_nxt;
-        if (f + 1 < NVF) vf_nxt = read_vf(f + 1);
-        if (f + 1 == NVF) r4 = fetch(u + 4);   // list entries of u+4, after the last LDS read
-        if (f == 0) {
-          // the last exponential pairs are complete, and 2 wait states separate
-          // their P writes from the first MFMA that reads them
+      for (int j = 0; j < 2 * NH; ++j) {
+        const int f = j / QT, qt = j % QT;
+        const int c = f / DT, dt = f % DT;
+        if (qt == 0 && f + 2 < NVF) vfr[f + 2] = read_vf(f + 2);
+        if (j == NH) {
+          // P chunk c = 1 complete before its first MFMA (2 wait states)
 #pragma unroll
-          for (int e = 0; e < PPM; ++e) {
-            const int pi = (NM - 1) * PPM + e;
-            pin_before(pw[pi / 8][pi % 8]);
-            pin_before(l_run[pi / 8]);
-          }
+          for (int q2 = 0; q2 < QT; ++q2)
+            pb[q2][1] = as_frag(make_uint4(pw[q2][4], pw[q2][5], pw[q2][6], pw[q2][7]));
           asm volatile("s_nop 1" ::: "memory");
+          // the row max reads S(u+1) from here on (8+ MFMAs after its last one)
+#pragma unroll
+          for (int t = 0; t < QT; ++t) asm volatile("" : "+v"(snext[t]));
         }
+        mma_o(o[qt][dt], vfr[f], pb[qt][c]);
+        if (j < NLD) load_fast(rk, i_u3, kslot(p ^ 1), true, j, part_k);
+        if (j < NH) {
+          // pairs k = 4..7 spread over the first half
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int j = f * QT + qt;
-          mma_o(o[qt][dt], vf_cur, pb[qt][c]);
-          if (j < NLD) load_fast(rk, i_u3, kslot(p ^ 1), true, j, part_k);
-          if (j == 2) {
-            // the row max of S(u+1) starts here, 12+ wait states after its last MFMA
-            asm volatile("s_nop 4" ::: "memory");
+          for (int e = 0; e < NP2; ++e) {
+            if (e * NH / NP2 == j) pair(4 + e);
+          }
+        } else {
+          // row max steps spread over the second half
+          const int jj = j - NH;
 #pragma unroll
-            for (int t = 0; t < QT; ++t) asm volatile("" : "+v"(snext[t]));
+          for (int e = 0; e < NRS; ++e) {
+            if (e * NH / NRS == jj) {
+#pragma unroll
+              for (int q2 = 0; q2 < QT; ++q2) rowmax_part(q2, e);
+            }
           }
         }
-        vf_cur = vf_nxt;
+        // K(u+2) fragments for the next step, read during the last MFMAs
+        if (j == 2 * NH - 4) {
+          const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(p));
+          tile_wait();   // K(u+2) landed
+#pragma unroll
+          for (int c2 = 0; c2 < KC; ++c2) kf[c2] = lds_frag(kt + (ka ^ (uint32_t)(c2 * 32)));
+        }
       }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) row_mx[qt] = mx[qt];
     };
 
     auto step = [&](auto par, auto full, int u, const Info& i_u3) {
       constexpr int p = decltype(par)::value;   // u & 1
       constexpr bool kFull = decltype(full)::value;
-      Raw r4;
+      const Raw r5 = fetch(u + 5);   // used two steps from now
       if constexpr (kDma) {
-        step_mma(par, u, i_u3, r4);
+        step_mma(par, u, i_u3);
       } else {
-        r4 = fetch(u + 4);
         load_tile(rv, i_u1, vslot(p ^ 1), false, full);
         bf16x8 pb[QT][2];
         qk(p ^ 1, sc[p ^ 1]);
@@ -689,7 +793,12 @@ void fwd_kernel(FwdArgs a) {
         load_tile(rk, i_u3, kslot(p ^ 1), true, full);
       }
       float mx[QT];
-      rowmax(sc[p ^ 1], i_u1, mx);
+      if constexpr (kDma) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) mx[qt] = row_mx[qt];
+      } else {
+        rowmax(sc[p ^ 1], i_u1, mx);
+      }
       if (u + 1 < nsub) {
         if constexpr (kDma) {
           // vector reads of O (rescale) 12+ wait states after the last P V MFMA
@@ -708,6 +817,7 @@ void fwd_kernel(FwdArgs a) {
       i_u1 = i_u2;
       i_u2 = info(u + 3, r3);
       r3 = r4;
+      r4 = r5;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
