@@ -716,16 +716,26 @@ void fwd_kernel(FwdArgs a) {
           case 1: r[2] = max3(x[8], x[9], x[10]); r[3] = max3(x[11], x[12], x[13]); pin_before(r[3]); break;
           case 2: r[0] = max3(r[0], r[1], x[6]); r[2] = max3(r[2], r[3], x[14]); pin_before(r[2]); break;
           case 3: {
-            r[0] = fmaxf(r[0], x[7]);
-            r[2] = fmaxf(r[2], x[15]);
+            r[0] = max3(r[0], x[7], x[7]);
+            r[2] = max3(r[2], x[15], x[15]);
             float m;
-            if constexpr (NBLK == 2) m = fmaxf(r[0] * a.scale_log2 + i_u1.bias[0], r[2] * a.scale_log2 + i_u1.bias[1]);
-            else m = fmaxf(r[0], r[2]) * a.scale_log2 + i_u1.bias[0];
+            if constexpr (NBLK == 2) {
+              const float m0 = r[0] * a.scale_log2 + i_u1.bias[0];
+              const float m1 = r[2] * a.scale_log2 + i_u1.bias[1];
+              m = max3(m0, m1, m1);
+            } else {
+              m = max3(r[0], r[2], r[2]) * a.scale_log2 + i_u1.bias[0];
+            }
             r[4] = m;
             pin_before(r[4]);
             break;
           }
-          default: mx[qt] = max_xor32(r[4]); pin_before(mx[qt]); break;
+          default: {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[4]), __float_as_uint(r[4]), false, false);
+            mx[qt] = max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+            pin_before(mx[qt]);
+            break;
+          }
         }
       };
       constexpr int NRS = 5;               // row max steps per q-tile
@@ -815,7 +825,7 @@ void fwd_kernel(FwdArgs a) {
       }
       i_u = i_u1;
       i_u1 = i_u2;
-      i_u2 = info(u + 3, r3);
+      i_u2 = i_u3;
       r3 = r4;
       r4 = r5;
     };
