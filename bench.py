@@ -40,14 +40,23 @@ def _args():
     return ap.parse_args()
 
 
+def code_digest(path_src):
+    """sha256 of a HIP source with `//` comments and blank lines removed (the code the counters measured)."""
+    out = []
+    for line in open(path_src, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            out.append(code)
+    return hashlib.sha256("\n".join(out).encode()).hexdigest()
+
+
 def _traffic(path_src, name):
-    """HBM bytes per forward launch from committed rocprofv3 counters, if the kernel is unchanged."""
+    """HBM bytes per forward launch from committed rocprofv3 counters, if the kernel code is unchanged."""
     f = os.path.join(ROOT, "profiles", f"traffic_fwd_{name}.json")
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
-    h = hashlib.sha256(open(path_src, "rb").read()).hexdigest()
-    if rec.get("forward_hip_sha256") != h:
+    if rec.get("forward_hip_code_sha256") != code_digest(path_src):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -8,25 +8,34 @@
 //
 // Work decomposition:
 //   * one workgroup = one wave = one (b, h, query block) of 32 or 64 rows.
-//     The wave may use up to 512 registers (one wave per SIMD), so the O^T
-//     accumulators and Q fragments of the whole query block, two score
-//     tiles and two key sub-tiles stay in registers, and every K/V byte read
-//     from LDS or L2 feeds all rows of the block;
+//     The wave may use up to 512 registers (one wave per SIMD): the Q
+//     fragments and the O^T accumulators of the whole query block live in
+//     AGPRs, the two score tiles and the softmax state in VGPRs, so every
+//     K/V byte read from LDS feeds all rows of the block;
 //   * the block's selected key blocks are walked in 32-key sub-tiles
 //     (16-key blocks are gathered two per sub-tile);
-//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: each lane
-//     owns one query column of a 32-row tile, so the running max, sum and
-//     rescale stay in the lane (one permlane32 swap joins the key halves);
-//   * K rows go from L2 straight into A-operand registers (16 bytes per lane
-//     per k chunk, no LDS), issued three sub-tiles ahead; V rows go to LDS by
-//     buffer-load DMA into a three-deep ring, issued two sub-tiles ahead, and
-//     are read back with the transposing LDS read as V^T A operands;
-//   * software pipeline per sub-tile u: the S(u+1) MFMAs are interleaved with
-//     the exponentials of S(u), and the P V MFMAs of u with the row max of
-//     S(u+1), so matrix cores and vector ALU overlap inside the wave;
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (issued as
+//     inline asm with fixed register classes, so the compiler never shuffles
+//     accumulators between register files): each lane owns one query column
+//     of a 32-row tile, so the running max, sum and rescale stay in the lane
+//     (one permlane32 swap joins the two key halves);
+//   * K and V sub-tiles go from HBM/L2 to LDS by buffer-load DMA into two
+//     slots each (K two sub-tiles ahead, V one ahead). A group of loads
+//     shares one scalar row offset and differs only in the literal
+//     immediate; the waits before LDS reads are explicit in-order vmcnt
+//     counts. K is read back with ds_read_b128, V^T with the transposing
+//     ds_read_b64_tr_b16, both from XOR-swizzled layouts;
+//   * the list entries (key block, log-weight) are fetched by vector loads
+//     five sub-tiles ahead and broadcast with readlane, so no scalar-cache
+//     wait ever blocks the tile loads;
+//   * software pipeline per sub-tile u: phase 1 issues the S(u+1) MFMAs with
+//     the exponentials of S(u) and the V(u+1) loads between them; phase 2
+//     issues the P V MFMAs of u with the rest of the exponentials, the row
+//     max of S(u+1) and the K(u+3) loads between them;
 //   * softmax in the log2 domain with lazy rescaling (the reference max moves
 //     only when a row max grows by more than 8), scale and per-block
-//     log-weight folded into one multiply-add.
+//     log-weight folded into one multiply-add, row sums by v_dot2 over the
+//     same bf16 P the P V product uses.
 #include "bsa_internal.h"
 
 namespace bsa {
