@@ -543,29 +543,33 @@ void fwd_kernel(FwdArgs a) {
   };
 
   // Vector-memory instructions retire in issue order, and every step issues
-  // them in the same order: its two list loads, the NLD V(u+1) loads (phase
-  // 1), the NLD K(u+3) loads (phase 2); a partial tile adds its own NLD loads
-  // before them.  When the V(u) fragments are read (late in phase 1) and when
-  // the K(u+2) fragments are read (late in phase 2), the tile they need was
-  // followed by at least 2 + 2 NLD other loads, so waiting until at most that
-  // many are outstanding is enough (and merely conservative after a partial
-  // tile).  In the prologue a tile is followed by two others (2 NLD loads).
-  auto tile_wait = [&]() {
-    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 + 2 * NLD) : "memory");
+  // them in the same order: its two list loads, the NLD V(u+1) loads (one
+  // after each of the first NLD MFMAs of phase 1), the NLD K(u+3) loads (one
+  // after each of the first NLD MFMAs of phase 2); a partial tile adds its own
+  // NLD loads before them.  A wait for a tile counts the loads issued after
+  // the tile's last one up to the wait: vmcnt(that count) lets the tile land,
+  // and is merely conservative after a partial tile (more loads were issued).
+  // In the prologue a tile is followed by two others (2 NLD loads).
+  auto tile_wait = [&](auto n) {
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory");
   };
+  static_assert(NLD <= KC && NLD <= 2 * DT * QT, "tile loads must fit in the MFMAs of a phase");
 
   // ---- pipeline ----
   // Step u (p = u & 1): sc[p] holds S(u) (masked, its max folded into
-  // m_run); K(u+1) is in K slot (u+1) % 2 and V(u) in V slot u % 2.
-  //   phase 1: S(u+1) MFMAs into sc[p^1], each followed by a pair of
-  //            exponentials of S(u) (P(u) and its row sums); V(u+1) loads into
-  //            V slot (u+1) % 2 (last read by step u-1) between them;
-  //   phase 2: P(u) V(u) MFMAs, with K(u+3) loads into K slot (u+1) % 2 (read
-  //            in phase 1) between them; the mask and row max of S(u+1) run
-  //            after the third of them;
+  // m_run); the K(u+1) fragments are in registers, K(u+2) is in K slot u % 2
+  // and V(u) in V slot u % 2.
+  //   phase 1: S(u+1) MFMAs into sc[p^1], with the exponentials of the first
+  //            half of S(u) (P(u) and its row sums) and the V(u+1) loads into
+  //            V slot (u+1) % 2 (last read by step u-1) between them; the
+  //            V(u) fragments are read from LDS from the last MFMAs on;
+  //   phase 2: P(u) V(u) MFMAs, with the second half of the exponentials, the
+  //            row max of S(u+1) and the K(u+3) loads into K slot (u+1) % 2
+  //            between them; the K(u+2) fragments are read during the last
+  //            MFMAs;
   //   then the rescale for S(u+1) if a row max grew past the tolerance.
   // Sub-tiles past the list load zeros and never reach O.  The waits for the
-  // tile loads are derived by the compiler from the LDS slot each read touches.
+  // tile loads are explicit vmcnt counts (see tile_wait).
   if (nsub > 0) {
     f32x16 sc[2][QT];
     Info i_u = info(0, fetch(0));   // sub-tile u
@@ -680,12 +684,16 @@ void fwd_kernel(FwdArgs a) {
       // ---- phase 1: pairs k = 0..3 of each q-tile (P chunk c = 0) ----
       constexpr int NM = KC * QT;          // MFMAs of S(u+1)
       constexpr int NP1 = 4;               // pair groups in phase 1 (k = 0..3)
+      // the first two V(u) fragments are read during the last MFMAs of phase
+      // 1, the others two ahead of their MFMAs; V(u) was followed by K(u+2),
+      // the list loads and the V(u+1) loads issued so far
+      constexpr int IV = NM > 4 ? NM - 4 : 0;
+      constexpr int NWV = NLD + 2 + (IV < NLD ? IV : NLD);
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         const int c = i / QT, qt2 = i % QT;
-        // the first two V(u) fragments are read during the last MFMAs of phase 1
-        if (i == NM - 4) {
-          tile_wait();   // V(u) landed
+        if (i == IV) {
+          tile_wait(std::integral_constant<int, NWV>{});   // V(u) landed
           vfr[0] = read_vf(0);
           if (NVF > 1) vfr[1] = read_vf(1);
         }
@@ -748,6 +756,8 @@ void fwd_kernel(FwdArgs a) {
         }
       };
       constexpr int NRS = 5;               // row max steps per q-tile
+      constexpr int JK = 2 * NH > 4 ? 2 * NH - 4 : 0;
+      constexpr int NWK = 2 + NLD + (JK + 1 < NLD ? JK + 1 : NLD);
 #pragma unroll
       for (int j = 0; j < 2 * NH; ++j) {
         const int f = j / QT, qt = j % QT;
@@ -782,10 +792,11 @@ void fwd_kernel(FwdArgs a) {
             }
           }
         }
-        // K(u+2) fragments for the next step, read during the last MFMAs
-        if (j == 2 * NH - 4) {
+        // K(u+2) fragments for the next step, read during the last MFMAs; K(u+2)
+        // was followed by the list loads, V(u+1) and the K(u+3) loads so far
+        if (j == JK) {
           const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(p));
-          tile_wait();   // K(u+2) landed
+          tile_wait(std::integral_constant<int, NWK>{});   // K(u+2) landed
 #pragma unroll
           for (int c2 = 0; c2 < KC; ++c2) kf[c2] = lds_frag(kt + (ka ^ (uint32_t)(c2 * 32)));
         }

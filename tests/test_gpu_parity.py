@@ -123,6 +123,15 @@ SMALL = {
     "ragged_f32_d64_q32_k16": tiny(text_len=19, frames=3, lh=7, lw=9, bq=32, bk=16, D=64, H=2,
                                   dtype="f32", mode="topk", topk=5, text_columns=True, centroids=4,
                                   grid=(2, 2), align=32),
+    "ragged_bf16_q32_k64": tiny(text_len=45, frames=5, lh=12, lw=16, bq=32, bk=64, D=128, H=2,
+                               dtype="bf16", mode="topk", topk=0, keep_ratio=0.4, centroids=8,
+                               grid=(2, 4), align=64),
+    "ragged_bf16_q32_k16_text": tiny(text_len=50, frames=4, lh=10, lw=14, bq=32, bk=16, D=128, H=2,
+                                    dtype="bf16", mode="topk", topk=0, keep_ratio=0.25, text_columns=True,
+                                    centroids=8, grid=(2, 4), align=32),
+    "ragged_bf16_d64_q32_k32_sample": tiny(text_len=0, frames=6, lh=10, lw=12, bq=32, bk=32, D=64, H=2,
+                                          dtype="bf16", mode="sample", topk=0, keep_ratio=0.3,
+                                          sample_seed=11, centroids=8, grid=(2, 4), align=32),
     "ragged_bf16_d64_sample_k64": tiny(text_len=0, frames=6, lh=10, lw=13, bq=64, bk=64, D=64, H=2,
                                       dtype="bf16", mode="sample", topk=0, keep_ratio=0.3, sample_seed=99,
                                       frame0_dense=False, centroids=8, grid=(2, 4), align=64),
