@@ -11,11 +11,13 @@
 //   A. all 512 threads compute the R x nkb float32 logits into LDS, each
 //      logit as a sequential non-fused multiply-add chain over D in
 //      ascending order (the library's contract, so the integer decisions
-//      that follow are bit-reproducible);
+//      that follow are bit-reproducible); a thread owns 8 rows x JT key
+//      blocks, so each q or k chunk it reads feeds several chains;
 //   B. each wave then owns one row at a time: radix select of the k-th
 //      largest logit (four 8-bit passes over a per-wave LDS histogram) and a
 //      ballot-ordered compaction for top-k; or exp / water-filling /
-//      Philox draws / log-weights for sampling.  Frame-0 rows skip straight
+//      Philox draws (one evaluation per four blocks) / log-weights for
+//      sampling.  Frame-0 rows skip straight
 //      to "all blocks"; text columns are OR-ed in.
 #include "bsa_internal.h"
 
@@ -78,7 +80,8 @@ __device__ __forceinline__ float exp_le0(float t) {
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011) -------------------
-__device__ __forceinline__ uint64_t philox_word(uint64_t c0, uint64_t c1, uint64_t k0, int word) {
+// The four 64-bit output words of counter (c0, c1, 0, 0) under key (k0, 0).
+__device__ __forceinline__ void philox4(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t (&x)[4]) {
   const uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
   const uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
   uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
@@ -91,7 +94,7 @@ __device__ __forceinline__ uint64_t philox_word(uint64_t c0, uint64_t c1, uint64
     const uint64_t n0 = hi1 ^ x1 ^ key0, n2 = hi0 ^ x3 ^ key1;
     x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
   }
-  return word == 0 ? x0 : word == 1 ? x1 : word == 2 ? x2 : x3;
+  x[0] = x0; x[1] = x1; x[2] = x2; x[3] = x3;
 }
 
 // ---- radix select of the k-th largest order key of a row ------------------
@@ -138,6 +141,8 @@ __device__ void radix_select(const float* zr, int n, int k, int* hist, uint32_t&
   T = prefix;
 }
 
+// JT: key blocks per thread in the logits phase (1, 2 or 4).
+template <int JT>
 __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
   __shared__ float zs[kZFloats];
   __shared__ float qs[kMaxRows * 128];
@@ -155,35 +160,66 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
   const int D = a.D;
 
   // ---- A. logits --------------------------------------------------------
+  // Each thread owns RT rows x JT key blocks; every wave of a row group reads
+  // the same q row chunk (an LDS broadcast) and its lanes' own k rows, so one
+  // 16-byte q read feeds 4 JT products and one k read 4 RT.  Rows past nrows
+  // see zero q rows and are not stored.
+  constexpr int RT = 8;
   const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
-  for (int e = tid; e < nrows * D; e += kMaskThreads) qs[e] = qsrc[e];
+  for (int e = tid; e < kMaxRows * D; e += kMaskThreads) qs[e] = e < nrows * D ? qsrc[e] : 0.0f;
   __syncthreads();
-  for (int j = tid; j < n; j += kMaskThreads) {
-    float acc[kMaxRows];
+  {
+    const int RG = (nrows + RT - 1) / RT;          // row groups (1 or 2)
+    const int WPG = kMaskWaves / RG;               // waves per row group
+    const int rg = wave / WPG;
+    const int gl = (wave % WPG) * 64 + lane;       // lane within the row group
+    const int slots = WPG * 64;                    // key blocks per pass and jj
+    const float* kbase = a.kp + (int64_t)bh * n * D;
+    const float* qrow = qs + rg * RT * D;
+    for (int base = 0; base < n; base += slots * JT) {
+      float acc[RT][JT];
+      const float* kr[JT];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0f;
-    const float* kr = a.kp + ((int64_t)bh * n + j) * D;
-    for (int d = 0; d < D; d += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
+      for (int jj = 0; jj < JT; ++jj) {
+        const int j = min(base + gl + jj * slots, n - 1);
+        kr[jj] = kbase + (int64_t)j * D;
 #pragma unroll
-      for (int r = 0; r < kMaxRows; ++r) {
-        if (r < nrows) {
-          const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.x, kv.x));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
+        for (int r = 0; r < RT; ++r) acc[r][jj] = 0.0f;
+      }
+      for (int d = 0; d < D; d += 4) {
+        float4 kv[JT];
+#pragma unroll
+        for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(qrow + r * D + d);
+#pragma unroll
+          for (int jj = 0; jj < JT; ++jj) {
+            float t = acc[r][jj];
+            t = __fadd_rn(t, __fmul_rn(qv.x, kv[jj].x));
+            t = __fadd_rn(t, __fmul_rn(qv.y, kv[jj].y));
+            t = __fadd_rn(t, __fmul_rn(qv.z, kv[jj].z));
+            t = __fadd_rn(t, __fmul_rn(qv.w, kv[jj].w));
+            acc[r][jj] = t;
+          }
         }
       }
-    }
-    const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) {
-      if (r < nrows) {
-        float z = __fmul_rn(acc[r], a.scale);
-        if (a.log_cluster) z = __fadd_rn(z, lc);
-        if (z == 0.0f) z = 0.0f;                // -0 -> +0
-        zs[r * n + j] = z;
+      for (int jj = 0; jj < JT; ++jj) {
+        const int j = base + gl + jj * slots;
+        if (j < n) {
+          const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const int row = rg * RT + r;
+            if (row < nrows) {
+              float z = __fmul_rn(acc[r][jj], a.scale);
+              if (a.log_cluster) z = __fadd_rn(z, lc);
+              if (z == 0.0f) z = 0.0f;                // -0 -> +0
+              zs[row * n + j] = z;
+            }
+          }
+        }
       }
     }
   }
@@ -298,6 +334,19 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
         ncap = wave_sum_int(__popc(cap));
       }
     }
+    // draws: counter j / 4 gives the top 24 bits of word j % 4 for block j;
+    // one Philox evaluation per counter, the draws staged (as 24-bit integers,
+    // exact in float) in the row's logit slots, which are no longer needed:
+    // e holds what follows from them
+    float* ur = zs + r * n;
+    for (int cc = lane; cc < (n + 3) / 4; cc += 64) {
+      uint64_t x[4];
+      philox4((uint64_t)rowid, (uint64_t)cc, a.seed, x);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (4 * cc + w < n) ur[4 * cc + w] = (float)(uint32_t)(x[w] >> 40);
+    }
+    wave_lds_sync();
     // pi, draws
     uint32_t selbits = 0;
     float pi[kMaxPerLane];
@@ -306,8 +355,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
       const int j = lane + 64 * mm;
       pi[mm] = (all_in || ((cap >> mm) & 1u)) ? 1.0f : __fmul_rn(c, e[mm]);
       if (mm < per && j < n) {
-        const uint64_t w = philox_word((uint64_t)rowid, (uint64_t)(j >> 2), a.seed, j & 3);
-        const float u = (float)(uint32_t)(w >> 40) * 5.9604644775390625e-08f;   // 2^-24
+        const float u = ur[j] * 5.9604644775390625e-08f;   // 2^-24
         if (u < pi[mm]) selbits |= 1u << mm;
       }
     }
@@ -346,7 +394,18 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream) {
   const int ngroups = (a.nqb + a.rows_per_group - 1) / a.rows_per_group;
   const int64_t grid = (int64_t)a.BH * ngroups;
-  hipLaunchKernelGGL(mask_kernel, dim3((unsigned)grid), dim3(kMaskThreads), 0, stream, a);
+  // key blocks per thread: the fewest passes x JT (per-lane work), ties to
+  // the larger JT (fewer q reads per product); two row groups of 256 lanes
+  const int slots = a.rows_per_group > 8 ? 256 : 512;
+  int jt = 1, best = 1 << 30;
+  for (int t : {1, 2, 4}) {
+    const int work = ((a.nkb + slots * t - 1) / (slots * t)) * t;
+    if (work <= best) { best = work; jt = t; }
+  }
+  const dim3 g((unsigned)grid), b(kMaskThreads);
+  if (jt == 4) hipLaunchKernelGGL(mask_kernel<4>, g, b, 0, stream, a);
+  else if (jt == 2) hipLaunchKernelGGL(mask_kernel<2>, g, b, 0, stream, a);
+  else hipLaunchKernelGGL(mask_kernel<1>, g, b, 0, stream, a);
   return hipGetLastError();
 }
 
