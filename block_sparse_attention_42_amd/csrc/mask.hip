@@ -11,7 +11,7 @@
 //   A. all 512 threads compute the R x nkb float32 logits into LDS, each
 //      logit as a sequential non-fused multiply-add chain over D in
 //      ascending order (the library's contract, so the integer decisions
-//      that follow are bit-reproducible); a thread owns 8 rows x JT key
+//      that follow are bit-reproducible); a thread owns all R rows x JT key
 //      blocks, so each q or k chunk it reads feeds several chains;
 //   B. each wave then owns one row at a time: radix select of the k-th
 //      largest logit (four 8-bit passes over a per-wave LDS histogram) and a
@@ -160,39 +160,32 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
   const int D = a.D;
 
   // ---- A. logits --------------------------------------------------------
-  // Each thread owns RT rows x JT key blocks; every wave of a row group reads
-  // the same q row chunk (an LDS broadcast) and its lanes' own k rows, so one
-  // 16-byte q read feeds 4 JT products and one k read 4 RT.  Rows past nrows
-  // see zero q rows and are not stored.
-  constexpr int RT = 8;
+  // Each thread owns all R rows x JT key blocks: every wave reads the same q
+  // row chunk (an LDS broadcast) and its lanes' own k rows, so one 16-byte q
+  // read feeds 4 JT products and one k read (the costly, scattered one) 4 R.
+  // Rows past nrows see zero q rows and are not stored.
   const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
   for (int e = tid; e < kMaxRows * D; e += kMaskThreads) qs[e] = e < nrows * D ? qsrc[e] : 0.0f;
   __syncthreads();
   {
-    const int RG = (nrows + RT - 1) / RT;          // row groups (1 or 2)
-    const int WPG = kMaskWaves / RG;               // waves per row group
-    const int rg = wave / WPG;
-    const int gl = (wave % WPG) * 64 + lane;       // lane within the row group
-    const int slots = WPG * 64;                    // key blocks per pass and jj
     const float* kbase = a.kp + (int64_t)bh * n * D;
-    const float* qrow = qs + rg * RT * D;
-    for (int base = 0; base < n; base += slots * JT) {
-      float acc[RT][JT];
+    for (int base = 0; base < n; base += kMaskThreads * JT) {
+      float acc[kMaxRows][JT];
       const float* kr[JT];
 #pragma unroll
       for (int jj = 0; jj < JT; ++jj) {
-        const int j = min(base + gl + jj * slots, n - 1);
+        const int j = min(base + tid + jj * kMaskThreads, n - 1);
         kr[jj] = kbase + (int64_t)j * D;
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r][jj] = 0.0f;
+        for (int r = 0; r < kMaxRows; ++r) acc[r][jj] = 0.0f;
       }
       for (int d = 0; d < D; d += 4) {
         float4 kv[JT];
 #pragma unroll
         for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(qrow + r * D + d);
+        for (int r = 0; r < kMaxRows; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
 #pragma unroll
           for (int jj = 0; jj < JT; ++jj) {
             float t = acc[r][jj];
@@ -206,17 +199,16 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
       }
 #pragma unroll
       for (int jj = 0; jj < JT; ++jj) {
-        const int j = base + gl + jj * slots;
+        const int j = base + tid + jj * kMaskThreads;
         if (j < n) {
           const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
 #pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const int row = rg * RT + r;
-            if (row < nrows) {
+          for (int r = 0; r < kMaxRows; ++r) {
+            if (r < nrows) {
               float z = __fmul_rn(acc[r][jj], a.scale);
               if (a.log_cluster) z = __fadd_rn(z, lc);
               if (z == 0.0f) z = 0.0f;                // -0 -> +0
-              zs[row * n + j] = z;
+              zs[r * n + j] = z;
             }
           }
         }
@@ -395,11 +387,10 @@ hipError_t launch_mask(const MaskArgs& a, hipStream_t stream) {
   const int ngroups = (a.nqb + a.rows_per_group - 1) / a.rows_per_group;
   const int64_t grid = (int64_t)a.BH * ngroups;
   // key blocks per thread: the fewest passes x JT (per-lane work), ties to
-  // the larger JT (fewer q reads per product); two row groups of 256 lanes
-  const int slots = a.rows_per_group > 8 ? 256 : 512;
+  // the larger JT (fewer q reads per product)
   int jt = 1, best = 1 << 30;
   for (int t : {1, 2, 4}) {
-    const int work = ((a.nkb + slots * t - 1) / (slots * t)) * t;
+    const int work = ((a.nkb + kMaskThreads * t - 1) / (kMaskThreads * t)) * t;
     if (work <= best) { best = work; jt = t; }
   }
   const dim3 g((unsigned)grid), b(kMaskThreads);
