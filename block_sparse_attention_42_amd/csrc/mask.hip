@@ -13,12 +13,13 @@
 //      ascending order (the library's contract, so the integer decisions
 //      that follow are bit-reproducible); a thread owns all R rows x JT key
 //      blocks, so each q or k chunk it reads feeds several chains;
-//   B. each wave then owns one row at a time: radix select of the k-th
-//      largest logit (four 8-bit passes over a per-wave LDS histogram) and a
-//      ballot-ordered compaction for top-k; or exp / water-filling /
-//      Philox draws (one evaluation per four blocks) / log-weights for
-//      sampling.  Frame-0 rows skip straight
-//      to "all blocks"; text columns are OR-ed in.
+//   B. each wave then owns one row at a time: for top-k, the k-th largest
+//      logit by a bitwise search over keys held in registers (rows of more
+//      than 2048 blocks: a radix select with four 8-bit passes over a
+//      per-wave LDS histogram), then a ballot-ordered compaction; for
+//      sampling, exp / water-filling / Philox draws (one evaluation per four
+//      blocks) / log-weights.  Frame-0 rows skip straight to "all blocks";
+//      text columns are OR-ed in.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -141,6 +142,64 @@ __device__ void radix_select(const float* zr, int n, int k, int* hist, uint32_t&
   T = prefix;
 }
 
+// ---- top-k of a row whose order keys fit in registers ----------------------
+// Slot mm of a lane holds block lane + 64 mm; empty slots hold 0, below the
+// key of every finite logit.  The k-th largest key T is found bit by bit from
+// the top: the largest T with at least k keys >= T, each count a sum of
+// ballot popcounts.  The search stops early once exactly k keys are >= T
+// (those are then the top k whatever the lower bits).  need = keys equal to
+// T that belong to the top k, which are the lowest-index ones.  Then the
+// ascending compaction, with the text columns OR-ed in.
+template <int PER>
+__device__ __forceinline__ void topk_row(const float* zr, int n, int k, int text_last, int lane, uint64_t below,
+                                         uint8_t* mrow, int32_t* irow, float* wrow, int32_t* cnt_out) {
+  uint32_t kk[PER];
+#pragma unroll
+  for (int mm = 0; mm < PER; ++mm) {
+    const int j = lane + 64 * mm;
+    kk[mm] = j < n ? order_key(zr[j]) : 0u;
+  }
+  uint32_t T = 0;
+  if (k < n) {
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = T | (1u << b);
+      int c = 0;
+#pragma unroll
+      for (int mm = 0; mm < PER; ++mm) c += __popcll(__ballot(kk[mm] >= cand));
+      if (c >= k) {
+        T = cand;
+        if (c == k) break;
+      }
+    }
+  }
+  int gt = 0;
+#pragma unroll
+  for (int mm = 0; mm < PER; ++mm) gt += __popcll(__ballot(kk[mm] > T));
+  const int need = k - gt;
+  int run_eq = 0, run_sel = 0;
+#pragma unroll
+  for (int mm = 0; mm < PER; ++mm) {
+    const int j = lane + 64 * mm;
+    const bool in = j < n;
+    const uint32_t key = kk[mm];
+    const bool eq = in && key == T;
+    const uint64_t beq = __ballot(eq);
+    const int eq_rank = run_eq + __popcll(beq & below);
+    bool sel = in && (key > T || (eq && eq_rank < need));
+    if (in && j <= text_last) sel = true;
+    const uint64_t bsel = __ballot(sel);
+    const int pos = run_sel + __popcll(bsel & below);
+    if (in && mrow) mrow[j] = sel ? 1 : 0;
+    if (sel) {
+      irow[pos] = j;
+      if (wrow) wrow[pos] = 0.0f;
+    }
+    run_eq += __popcll(beq);
+    run_sel += __popcll(bsel);
+  }
+  if (lane == 0) *cnt_out = run_sel;
+}
+
 // JT: key blocks per thread in the logits phase (1, 2 or 4).
 template <int JT>
 __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
@@ -238,7 +297,22 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
     }
     const float* zr = zs + r * n;
 
+    if (a.mode == 0 && n <= 64 * kMaxPerLane) {
+      int P = 64;
+      while (P < n) P <<= 1;
+      int32_t* co = a.cnt + rowid;
+      switch (P / 64) {
+        case 1: topk_row<1>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+        case 2: topk_row<2>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+        case 4: topk_row<4>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+        case 8: topk_row<8>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+        case 16: topk_row<16>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+        default: topk_row<32>(zr, n, a.topk, a.text_last, lane, below, mrow, irow, wrow, co); break;
+      }
+      continue;
+    }
     if (a.mode == 0) {
+      // rows longer than the register budget: radix select over LDS
       uint32_t T;
       int need;
       radix_select(zr, n, a.topk, hist, T, need);

@@ -195,6 +195,24 @@ def test_full_size_sampled_rows(name):
     _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qbl)
 
 
+def test_long_rows_top_k_radix_select():
+    """Rows of more than 2048 key blocks take the LDS radix-select path of the mask kernel."""
+    w = tiny(text_len=10, frames=2, lh=128, lw=130, bq=64, bk=16, D=64, H=1, dtype="bf16", mode="topk",
+             topk=0, keep_ratio=0.02, text_columns=True, frame0_dense=False, centroids=16, grid=(4, 4),
+             align=64)
+    g = geometry_of(w)
+    assert g.nkb > 2048
+    q, k, v = inputs_of(w)
+    r = run_gpu(w, q, k, v)
+    oqp = oracle.pool_blocks(q, g.S, g.q_block)
+    okp = oracle.pool_blocks(k, g.S, g.k_block)
+    assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w))
+    rows = [(0, 0, i) for i in range(g.nqb)]
+    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, {(0, 0): [0, 1, g.nqb // 2, g.nqb - 1]})
+
+
 def test_forward_arbitrary_lists_weights_and_nan_pads():
     w = tiny(text_len=21, frames=4, lh=9, lw=11, bq=64, bk=16, D=128, H=3, dtype="bf16", align=64,
              centroids=4, grid=(2, 2))
