@@ -295,11 +295,16 @@ void fwd_kernel(FwdArgs a) {
   };
   auto fetch = [&](int u) {
     const int b = lane < NBLK ? lane : 0;
-    const int pos = (u * SUB + b * PART) / BK;
-    const uint32_t off = (uint32_t)min(pos, max(cnt - 1, 0)) * 4u;   // every row has nkb >= 1 slots
+    const uint32_t pos = (uint32_t)(u * SUB + b * PART) / (uint32_t)BK;
+    const uint32_t off = min(pos, (uint32_t)max(cnt - 1, 0)) * 4u;   // every row has nkb >= 1 slots
     Raw r;
-    r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)off, 0, 0);
-    r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+    if constexpr (NBLK == 1) {   // one entry for all lanes: a scalar offset
+      r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, 0, (int)off, 0);
+      r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, 0, (int)off, 0);
+    } else {
+      r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)off, 0, 0);
+      r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+    }
     return r;
   };
   auto info = [&](int u, const Raw& r) {
@@ -309,13 +314,29 @@ void fwd_kernel(FwdArgs a) {
       const int g = u * SUB + b * PART;
       const int pos = g / BK;
       const int jr = __builtin_amdgcn_readlane(r.j, b);
-      const int j = (pos < cnt && jr >= 0 && jr < a.nkb) ? jr : -1;
-      const int key0 = j * BK + g % BK;
-      si.key0[b] = j >= 0 ? key0 : 0;
-      si.valid[b] = j >= 0 ? min(max(S32 - key0, 0), PART) : 0;
+      const bool ok = pos < cnt && (uint32_t)jr < (uint32_t)a.nkb;
+      const int key0 = jr * BK + g % BK;
+      si.key0[b] = ok ? key0 : 0;
+      // keys of the part before the end of the sequence, in [0, PART]
+      const int rest = S32 - key0;
+      si.valid[b] = ok ? (rest < PART ? (rest > 0 ? rest : 0) : PART) : 0;
       const float w = has_w ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(r.w, b)) : 0.0f;
-      si.bias[b] = j >= 0 ? w * 1.4426950408889634f : 0.0f;
+      si.bias[b] = ok ? w * 1.4426950408889634f : 0.0f;
     }
+    return si;
+  };
+  // A 64-key block spans two sub-tiles: the list entry of an odd sub-tile is
+  // that of the even one before it, so even steps fetch nothing and the
+  // second sub-tile's geometry follows from the first's.
+  constexpr bool kPair = BK == 2 * SUB;
+  auto info_second = [&](const Info& first) {
+    Info si;
+    const bool ok = first.valid[0] > 0;   // a listed block has keys in its first half
+    const int key0 = first.key0[0] + SUB;
+    const int rest = S32 - key0;
+    si.key0[0] = ok ? key0 : 0;
+    si.valid[0] = ok ? (rest < SUB ? (rest > 0 ? rest : 0) : SUB) : 0;
+    si.bias[0] = first.bias[0];
     return si;
   };
   auto is_full = [&](const Info& si) {
@@ -441,10 +462,12 @@ void fwd_kernel(FwdArgs a) {
   };
 
   float m_run[QT], l_run[QT];
+  float thr[QT];   // m_run + kTau: a row max above it moves the reference
   f32x16 o[QT][DT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = -INFINITY;
+    thr[qt] = -INFINITY;
     l_run[qt] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
@@ -455,13 +478,14 @@ void fwd_kernel(FwdArgs a) {
   auto rescale = [&](const float (&mx)[QT]) {
     bool grow = false;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > m_run[qt] + kTau;
+    for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > thr[qt];
     if (__any(grow)) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float m_new = mx[qt] > m_run[qt] + kTau ? mx[qt] : m_run[qt];
+        const float m_new = mx[qt] > thr[qt] ? mx[qt] : m_run[qt];
         const float alpha = fast_exp2(m_run[qt] - (m_new == -INFINITY ? 0.0f : m_new));
         m_run[qt] = m_new;
+        thr[qt] = m_new + kTau;
         l_run[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -543,7 +567,8 @@ void fwd_kernel(FwdArgs a) {
   };
 
   // Vector-memory instructions retire in issue order, and every step issues
-  // them in the same order: its two list loads, the NLD V(u+1) loads (one
+  // them in the same order: its list loads (two, none in the even steps of
+  // 64-key blocks), the NLD V(u+1) loads (one
   // after each of the first NLD MFMAs of phase 1), the NLD K(u+3) loads (one
   // after each of the first NLD MFMAs of phase 2); a partial tile adds its own
   // NLD loads before them.  A wait for a tile counts the loads issued after
@@ -688,7 +713,8 @@ void fwd_kernel(FwdArgs a) {
       // 1, the others two ahead of their MFMAs; V(u) was followed by K(u+2),
       // the list loads and the V(u+1) loads issued so far
       constexpr int IV = NM > 4 ? NM - 4 : 0;
-      constexpr int NWV = NLD + 2 + (IV < NLD ? IV : NLD);
+      constexpr int NF = (kPair && p == 0) ? 0 : 2;   // list loads of this step
+      constexpr int NWV = NLD + NF + (IV < NLD ? IV : NLD);
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         const int c = i / QT, qt2 = i % QT;
@@ -757,7 +783,7 @@ void fwd_kernel(FwdArgs a) {
       };
       constexpr int NRS = 5;               // row max steps per q-tile
       constexpr int JK = 2 * NH > 4 ? 2 * NH - 4 : 0;
-      constexpr int NWK = 2 + NLD + (JK + 1 < NLD ? JK + 1 : NLD);
+      constexpr int NWK = NF + NLD + (JK + 1 < NLD ? JK + 1 : NLD);
 #pragma unroll
       for (int j = 0; j < 2 * NH; ++j) {
         const int f = j / QT, qt = j % QT;
@@ -808,7 +834,11 @@ void fwd_kernel(FwdArgs a) {
     auto step = [&](auto par, auto full, int u, const Info& i_u3) {
       constexpr int p = decltype(par)::value;   // u & 1
       constexpr bool kFull = decltype(full)::value;
-      const Raw r5 = fetch(u + 5);   // used two steps from now
+      // list entry of sub-tile u + 5, used two steps from now (the same as
+      // that of u + 4 when a block spans two sub-tiles and u is even)
+      Raw r5;
+      if constexpr (kPair && p == 0) r5 = r4;
+      else r5 = fetch(u + 5);
       if constexpr (kDma) {
         step_mma(par, u, i_u3);
       } else {
@@ -834,7 +864,7 @@ void fwd_kernel(FwdArgs a) {
           // vector reads of O (rescale) 12+ wait states after the last P V MFMA
           bool grow = false;
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > m_run[qt] + kTau;
+          for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > thr[qt];
           if (__any(grow)) {
             fence_o();
             rescale(mx);
@@ -852,7 +882,9 @@ void fwd_kernel(FwdArgs a) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     auto step_any = [&](auto par, int u) {
-      const Info i_u3 = info(u + 3, r3);
+      Info i_u3;
+      if constexpr (kPair && decltype(par)::value == 0) i_u3 = info_second(i_u2);   // u + 3 odd
+      else i_u3 = info(u + 3, r3);
       if constexpr (kDma) {
         step(par, std::true_type{}, u, i_u3);   // partial tiles are handled inside
       } else {
