@@ -2,7 +2,8 @@
 
 Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py``; the library never imports, links or runs it.  See
-``oracle/reference.py`` for the definitions and the pages they follow.
+``oracle/reference.py`` for the definitions and the pages they follow, and
+``oracle/cluster_select.py`` for the intra-block clustering selector.
 """
 from .reference import *  # noqa: F401,F403
 from .reference import (Geometry, MaskParams, attention, attention_head, block_logits,  # noqa: F401
@@ -10,3 +11,5 @@ from .reference import (Geometry, MaskParams, attention, attention_head, block_l
                         philox4x64_10, pool_blocks, sample_uniforms, select_sample,
                         select_topk, topk_count, score_scale, forward_scale,
                         log_cluster_table)
+from .cluster_select import (block_softmax, cluster_importance, kmeans_block,  # noqa: F401
+                             select_blocks, select_sample_weights, water_fill)
