@@ -26,7 +26,8 @@ from . import _lib
 from ._lib import BsaError
 
 __all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
-           "bsa_build_mask", "bsa_forward", "library_path"]
+           "bsa_build_mask", "bsa_forward", "bsa_cluster_importance", "bsa_select_blocks",
+           "library_path"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -156,6 +157,50 @@ def bsa_build_mask(q_pooled: torch.Tensor, k_pooled: torch.Tensor, g: Geometry, 
     _lib.check(_lib.lib().bsa_build_mask(_ptr(q_pooled), _ptr(k_pooled), ctypes.byref(g.c()),
                                          ctypes.byref(p.c()), _ptr(mask), _ptr(cnt), _ptr(idx),
                                          _ptr(logw), _stream(stream)))
+    return mask, cnt, idx, logw
+
+
+def bsa_cluster_importance(q: torch.Tensor, k_pooled: torch.Tensor, g: Geometry, n_clusters: int = 4,
+                           iters: int = 3, log_cluster: bool = False, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Block importance [B,H,nqb,nkb] float32 from k-means representatives of each query block."""
+    d = bsa_derive(g)
+    nqb, nkb = d["nqb"], d["nkb"]
+    _need(q, "q", (g.B, g.H, g.seq_alloc, g.head_dim))
+    _need(k_pooled, "k_pooled", (g.B, g.H, nkb, g.head_dim), torch.float32, q.device)
+    if out is None:
+        out = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.float32, device=q.device)
+    _need(out, "importance", (g.B, g.H, nqb, nkb), torch.float32, q.device)
+    _lib.check(_lib.lib().bsa_cluster_importance(_ptr(q), _dtype_code(q), _ptr(k_pooled), ctypes.byref(g.c()),
+                                                 int(n_clusters), int(iters), 1 if log_cluster else 0,
+                                                 _ptr(out), _stream(stream)))
+    return out
+
+
+def bsa_select_blocks(importance: torch.Tensor, g: Geometry, p: MaskParams, want_mask: bool = True,
+                      want_logw: Optional[bool] = None, out=None, stream=None):
+    """Selection from an importance matrix -> (mask, kv_cnt, kv_idx, log_w) as bsa_build_mask."""
+    d = bsa_derive(g, p)
+    nqb, nkb = d["nqb"], d["nkb"]
+    dev = importance.device
+    _need(importance, "importance", (g.B, g.H, nqb, nkb), torch.float32)
+    if want_logw is None:
+        want_logw = p.mode == "sample"
+    if out is None:
+        mask = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
+        cnt = torch.empty((g.B, g.H, nqb), dtype=torch.int32, device=dev)
+        idx = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.int32, device=dev)
+        logw = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.float32, device=dev) if want_logw else None
+    else:
+        mask, cnt, idx, logw = out
+    if mask is not None:
+        _need(mask, "mask", (g.B, g.H, nqb, nkb), torch.uint8, dev)
+    _need(cnt, "kv_cnt", (g.B, g.H, nqb), torch.int32, dev)
+    _need(idx, "kv_idx", (g.B, g.H, nqb, nkb), torch.int32, dev)
+    if logw is not None:
+        _need(logw, "log_w", (g.B, g.H, nqb, nkb), torch.float32, dev)
+    _lib.check(_lib.lib().bsa_select_blocks(_ptr(importance), ctypes.byref(g.c()), ctypes.byref(p.c()),
+                                            _ptr(mask), _ptr(cnt), _ptr(idx), _ptr(logw), _stream(stream)))
     return mask, cnt, idx, logw
 
 

@@ -15,6 +15,7 @@ BSA_SELECT_TOPK = 0
 BSA_SELECT_SAMPLE = 1
 
 EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward",
+            "bsa_cluster_importance", "bsa_select_blocks",
             "bsa_status_string", "bsa_last_error", "bsa_abi_version"]
 
 
@@ -59,7 +60,11 @@ def lib():
         L.bsa_pool_blocks.argtypes = [P, ctypes.c_int32, G, ctypes.c_int32, P, P]
         L.bsa_build_mask.argtypes = [P, P, G, M, P, P, P, P, P]
         L.bsa_forward.argtypes = [P, P, P, ctypes.c_int32, G, P, P, P, ctypes.c_float, P, P, P]
-        for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_abi_version"):
+        L.bsa_cluster_importance.argtypes = [P, ctypes.c_int32, P, G, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, P, P]
+        L.bsa_select_blocks.argtypes = [P, G, M, P, P, P, P, P]
+        for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_abi_version",
+                  "bsa_cluster_importance", "bsa_select_blocks"):
             getattr(L, f).restype = ctypes.c_int32
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p

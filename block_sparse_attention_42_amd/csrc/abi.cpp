@@ -207,8 +207,96 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
   a.frame0_last = p->frame0_dense ? d.f0_last : -1;
   a.text_last = p->text_columns ? d.text_last : -1;
   a.seed = p->seed;
+  a.imp = nullptr;
   hipError_t e = bsa::launch_mask(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_pooled,
+                                  const bsa_geometry* g, int32_t n_clusters, int32_t iters,
+                                  int32_t log_cluster, float* importance, void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (dtype != BSA_DTYPE_BF16 && dtype != BSA_DTYPE_F32)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (!q || !k_pooled || !importance)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_pooled and importance must not be NULL");
+  if (!aligned16(q) || !aligned16(k_pooled) || !aligned16(importance))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (n_clusters < 1 || n_clusters > 8)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "n_clusters %d must be in 1..8", n_clusters);
+  if (iters < 0 || iters > 16) return fail(BSA_ERR_INVALID_ARGUMENT, "iters %d must be in 0..16", iters);
+  if (d.nkb > 8192 || (int64_t)n_clusters * d.nkb > 16384)
+    return fail(BSA_ERR_UNSUPPORTED, "n_clusters * nkb = %lld > 16384 (or nkb > 8192)",
+                (long long)n_clusters * d.nkb);
+  if ((int64_t)g->B * g->H * d.nqb > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+  bsa::ImpArgs a;
+  a.q = q;
+  a.kp = k_pooled;
+  a.imp = importance;
+  a.seq_alloc = g->seq_alloc;
+  a.S = d.S;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.D = g->head_dim;
+  a.q_block = g->q_block;
+  a.C = n_clusters;
+  a.T = iters;
+  a.scale = (float)(1.0 / std::sqrt((double)g->head_dim));
+  a.log_cluster = log_cluster ? 1 : 0;
+  const int64_t n_last = d.S - (int64_t)(d.nkb - 1) * g->k_block;
+  a.ln_full = (float)std::log((double)g->k_block);
+  a.ln_last = (float)std::log((double)n_last);
+  if (bsa::importance_lds_bytes(a) > 160 * 1024) return fail(BSA_ERR_UNSUPPORTED, "LDS budget exceeded");
+  hipError_t e = bsa::launch_importance(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "importance launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g, const bsa_mask_params* p,
+                             uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, float* log_w,
+                             void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  s = check_params(p, d);
+  if (s != BSA_OK) return s;
+  if (!importance || !kv_cnt || !kv_idx)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "importance, kv_cnt and kv_idx must not be NULL");
+  if (!aligned16(importance) || !aligned16(kv_cnt) || !aligned16(kv_idx) ||
+      (mask && !aligned16(mask)) || (log_w && !aligned16(log_w)))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (p->mode == BSA_SELECT_SAMPLE && !log_w)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "sampling needs log_w");
+  const int32_t nkb_max = p->mode == BSA_SELECT_SAMPLE ? 2048 : 8192;
+  if (d.nkb > nkb_max)
+    return fail(BSA_ERR_UNSUPPORTED, "nkb %d > %d for this selection mode", d.nkb, nkb_max);
+  bsa::MaskArgs a = {};
+  a.imp = importance;
+  a.mask = mask;
+  a.cnt = kv_cnt;
+  a.idx = kv_idx;
+  a.logw = log_w;
+  a.H = g->H;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.D = g->head_dim;
+  int rows = 32768 / d.nkb;
+  a.rows_per_group = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
+  a.mode = p->mode;
+  a.topk = topk_of(p, d.nkb);
+  a.expected = (float)(p->keep_ratio * (double)d.nkb);
+  a.frame0_first = p->frame0_dense ? d.f0_first : -1;
+  a.frame0_last = p->frame0_dense ? d.f0_last : -1;
+  a.text_last = p->text_columns ? d.text_last : -1;
+  a.seed = p->seed;
+  hipError_t e = bsa::launch_mask(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "selection launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -41,6 +41,22 @@ struct MaskArgs {
   int32_t frame0_first, frame0_last;   // -1 if off
   int32_t text_last;                   // -1 if off
   uint64_t seed;
+  const float* imp;   // [BH, nqb, nkb] block importance to select from (qp, kp unused), or null
+};
+
+// Launch arguments of the block-importance kernel (intra-block clusters).
+struct ImpArgs {
+  const void* q;      // [BH, seq_alloc, D]
+  const float* kp;    // [BH, nkb, D]
+  float* imp;         // [BH, nqb, nkb]
+  int64_t seq_alloc;
+  int64_t S;
+  int32_t BH, nqb, nkb, D, q_block;
+  int32_t C, T;       // clusters per query block (1..8), Lloyd rounds
+  float scale;        // fp32(1/sqrt(D))
+  int32_t log_cluster;
+  float ln_full;      // fp32(ln k_block)
+  float ln_last;      // fp32(ln n_last)
 };
 
 // Launch arguments of the sparse forward kernel.
@@ -74,6 +90,8 @@ inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int
 
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
+size_t importance_lds_bytes(const ImpArgs& a);
+hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 }  // namespace bsa

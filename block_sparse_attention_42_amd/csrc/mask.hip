@@ -21,6 +21,7 @@
 //      blocks) / log-weights.  Frame-0 rows skip straight to "all blocks";
 //      text columns are OR-ed in.
 #include "bsa_internal.h"
+#include "spec_math.h"
 
 namespace bsa {
 namespace {
@@ -47,37 +48,6 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
   return v;
-}
-
-// ---- e^t for t <= 0, float32, fixed operation sequence ----------------------
-// Cody & Waite argument reduction (W. J. Cody, W. Waite, "Software Manual for
-// the Elementary Functions", 1980): n = round(t*log2 e), x = t - n*ln2 with
-// ln2 split into a 15-bit high part (n*ln2_hi exact) and a low part; e^x by
-// the degree-7 Taylor polynomial (Horner, no fused multiply-add); result
-// r * 2^n.  Arguments with t*log2 e < -125 give 0.
-__device__ __forceinline__ float exp_le0(float t) {
-  const float kLog2e = (float)1.4426950408889634;
-  const float kLn2Hi = (float)0.693145751953125;
-  const float kLn2Lo = (float)(0.6931471805599453 - 0.693145751953125);
-  const float c0 = (float)(1.0 / 1.0), c1 = (float)(1.0 / 1.0), c2 = (float)(1.0 / 2.0);
-  const float c3 = (float)(1.0 / 6.0), c4 = (float)(1.0 / 24.0), c5 = (float)(1.0 / 120.0);
-  const float c6 = (float)(1.0 / 720.0), c7 = (float)(1.0 / 5040.0);
-  float y = __fmul_rn(t, kLog2e);
-  const bool flush = y < -125.0f;
-  if (flush) { t = 0.0f; y = 0.0f; }
-  const float n = floorf(__fadd_rn(y, 0.5f));
-  float x = __fsub_rn(t, __fmul_rn(n, kLn2Hi));
-  x = __fsub_rn(x, __fmul_rn(n, kLn2Lo));
-  float r = c7;
-  r = __fadd_rn(__fmul_rn(r, x), c6);
-  r = __fadd_rn(__fmul_rn(r, x), c5);
-  r = __fadd_rn(__fmul_rn(r, x), c4);
-  r = __fadd_rn(__fmul_rn(r, x), c3);
-  r = __fadd_rn(__fmul_rn(r, x), c2);
-  r = __fadd_rn(__fmul_rn(r, x), c1);
-  r = __fadd_rn(__fmul_rn(r, x), c0);
-  const float out = ldexpf(r, (int)n);
-  return flush ? 0.0f : out;
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011) -------------------
@@ -218,56 +188,62 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
   const int n = a.nkb;
   const int D = a.D;
 
-  // ---- A. logits --------------------------------------------------------
+  // ---- A. logits (or the given importance rows) ---------------------------
   // Each thread owns all R rows x JT key blocks: every wave reads the same q
   // row chunk (an LDS broadcast) and its lanes' own k rows, so one 16-byte q
   // read feeds 4 JT products and one k read (the costly, scattered one) 4 R.
   // Rows past nrows see zero q rows and are not stored.
-  const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
-  for (int e = tid; e < kMaxRows * D; e += kMaskThreads) qs[e] = e < nrows * D ? qsrc[e] : 0.0f;
-  __syncthreads();
-  {
-    const float* kbase = a.kp + (int64_t)bh * n * D;
-    for (int base = 0; base < n; base += kMaskThreads * JT) {
-      float acc[kMaxRows][JT];
-      const float* kr[JT];
+  if (a.imp) {
+    // selection from a given importance matrix: its rows are the scores
+    const float* src = a.imp + ((int64_t)bh * a.nqb + i0) * n;
+    for (int e = tid; e < nrows * n; e += kMaskThreads) zs[e] = src[e];
+  } else {
+    const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
+    for (int e = tid; e < kMaxRows * D; e += kMaskThreads) qs[e] = e < nrows * D ? qsrc[e] : 0.0f;
+    __syncthreads();
+    {
+      const float* kbase = a.kp + (int64_t)bh * n * D;
+      for (int base = 0; base < n; base += kMaskThreads * JT) {
+        float acc[kMaxRows][JT];
+        const float* kr[JT];
 #pragma unroll
-      for (int jj = 0; jj < JT; ++jj) {
-        const int j = min(base + tid + jj * kMaskThreads, n - 1);
-        kr[jj] = kbase + (int64_t)j * D;
+        for (int jj = 0; jj < JT; ++jj) {
+          const int j = min(base + tid + jj * kMaskThreads, n - 1);
+          kr[jj] = kbase + (int64_t)j * D;
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) acc[r][jj] = 0.0f;
-      }
-      for (int d = 0; d < D; d += 4) {
-        float4 kv[JT];
-#pragma unroll
-        for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
-#pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
-#pragma unroll
-          for (int jj = 0; jj < JT; ++jj) {
-            float t = acc[r][jj];
-            t = __fadd_rn(t, __fmul_rn(qv.x, kv[jj].x));
-            t = __fadd_rn(t, __fmul_rn(qv.y, kv[jj].y));
-            t = __fadd_rn(t, __fmul_rn(qv.z, kv[jj].z));
-            t = __fadd_rn(t, __fmul_rn(qv.w, kv[jj].w));
-            acc[r][jj] = t;
-          }
+          for (int r = 0; r < kMaxRows; ++r) acc[r][jj] = 0.0f;
         }
-      }
+        for (int d = 0; d < D; d += 4) {
+          float4 kv[JT];
 #pragma unroll
-      for (int jj = 0; jj < JT; ++jj) {
-        const int j = base + tid + jj * kMaskThreads;
-        if (j < n) {
-          const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
+          for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
 #pragma unroll
           for (int r = 0; r < kMaxRows; ++r) {
-            if (r < nrows) {
-              float z = __fmul_rn(acc[r][jj], a.scale);
-              if (a.log_cluster) z = __fadd_rn(z, lc);
-              if (z == 0.0f) z = 0.0f;                // -0 -> +0
-              zs[r * n + j] = z;
+            const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
+#pragma unroll
+            for (int jj = 0; jj < JT; ++jj) {
+              float t = acc[r][jj];
+              t = __fadd_rn(t, __fmul_rn(qv.x, kv[jj].x));
+              t = __fadd_rn(t, __fmul_rn(qv.y, kv[jj].y));
+              t = __fadd_rn(t, __fmul_rn(qv.z, kv[jj].z));
+              t = __fadd_rn(t, __fmul_rn(qv.w, kv[jj].w));
+              acc[r][jj] = t;
+            }
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < JT; ++jj) {
+          const int j = base + tid + jj * kMaskThreads;
+          if (j < n) {
+            const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+            for (int r = 0; r < kMaxRows; ++r) {
+              if (r < nrows) {
+                float z = __fmul_rn(acc[r][jj], a.scale);
+                if (a.log_cluster) z = __fadd_rn(z, lc);
+                if (z == 0.0f) z = 0.0f;                // -0 -> +0
+                zs[r * n + j] = z;
+              }
             }
           }
         }
@@ -362,7 +338,8 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
 #pragma unroll
     for (int mm = 0; mm < kMaxPerLane; ++mm) {
       const int j = lane + 64 * mm;
-      e[mm] = (mm < per && j < n) ? exp_le0(__fsub_rn(zr[j], m)) : 0.0f;
+      // weights in proportion to exp(z - max z), or the given importance
+      e[mm] = (mm < per && j < n) ? (a.imp ? zr[j] : exp_le0(__fsub_rn(zr[j], m))) : 0.0f;
     }
     const float E = a.expected;
     uint32_t cap = 0;

@@ -11,7 +11,10 @@
  *      sampling, query blocks overlapping frame 0 forced dense, optional text
  *      columns, and the compacted per-row block lists  (bsa_build_mask);
  *   3. exact attention on the selected blocks only, with online softmax and
- *      an optional additive per-block log-weight  (bsa_forward).
+ *      an optional additive per-block log-weight  (bsa_forward);
+ *   and, as a finer selector, block importance from k-means representatives
+ *   of each query block (bsa_cluster_importance) with selection from any
+ *   importance matrix (bsa_select_blocks).
  *
  * Pages followed (title; section):
  *   - "Attention matrix view: make only frame-0 query rows dense": sec. 1
@@ -177,6 +180,53 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
                        const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
                        const float* log_w, float softmax_scale, void* out, float* lse,
                        void* stream);
+
+/* Intra-block clustering selector, step 1: block importance (AB-Attention
+ * page, TL;DR item 1 and the flowchart's intra-block cluster node: queries
+ * are clustered only inside their own query block; EG-Sparse page Eq. 2 for
+ * the cluster-size-weighted softmax of a representative).
+ *   q:          [B, H, seq_alloc, D] of `dtype` (the raw queries).
+ *   k_pooled:   [B, H, nkb, D] float32 (bsa_pool_blocks with k_block).
+ *   n_clusters: C in 1..8; a block of n < C valid tokens uses n clusters.
+ *   iters:      Lloyd rounds T in 0..16.
+ *   log_cluster: add fp32(ln n_j) to every logit (nonzero) or not.
+ *   importance: [B, H, nqb, nkb] float32, written.
+ *   Per query block: k-means of its valid tokens (squared Euclidean
+ *   distance, sequential non-fused float32 chain over the channels; initial
+ *   centroid c = token floor(c n / C); a token joins the lowest-index nearest
+ *   centroid; an update replaces each non-empty centroid by the mean of its
+ *   tokens, summed in ascending token order; T rounds, then one final
+ *   assignment gives the sizes m_c).  For each non-empty cluster, logits z
+ *   against every k̄_j exactly as in bsa_build_mask, e_j = exp(z_j - max z)
+ *   by a fixed float32 sequence (Cody-Waite reduction, degree-7 Taylor
+ *   polynomial), P_c,j = e_j / (sum of e by a halving tree over the row
+ *   padded to a power of two).  importance_j = sum over clusters, ascending,
+ *   of fl32(fl32(m_c / n) * P_c,j): the expected attention mass a query of
+ *   the block puts on key block j.  Bit-reproducible; each row sums to 1
+ *   within rounding.  With C = 1 and T >= 1 it is P' of the pooled block.
+ *   Limits: C * nkb <= 16384 and nkb <= 8192 (BSA_ERR_UNSUPPORTED beyond). */
+bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_pooled,
+                                  const bsa_geometry* g, int32_t n_clusters, int32_t iters,
+                                  int32_t log_cluster, float* importance, void* stream);
+
+/* Intra-block clustering selector, step 2: selection from an importance
+ * matrix (AB-Attention page, TL;DR item 2: blocks sampled in proportion to
+ * importance and reweighted by the inverse inclusion probability; frame-0
+ * page secs. 4, 6, 7 for the overrides).
+ *   importance: [B, H, nqb, nkb] float32, finite, >= 0 (e.g. from
+ *               bsa_cluster_importance).
+ *   p:          as for bsa_build_mask; log_cluster is ignored (already in
+ *               the importance).  TOPK keeps the k largest importances of a
+ *               row (lower index first among equals); SAMPLE draws each block
+ *               with inclusion probability pi_j = min(1, c * importance_j),
+ *               sum pi = keep_ratio * nkb, exactly as bsa_build_mask does
+ *               from exp(z - max z); the safeguard keeps the first block of
+ *               largest importance.
+ *   mask, kv_cnt, kv_idx, log_w: as for bsa_build_mask.
+ *   Limits as for bsa_build_mask. */
+bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g,
+                             const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
+                             int32_t* kv_idx, float* log_w, void* stream);
 
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);

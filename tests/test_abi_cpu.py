@@ -106,6 +106,22 @@ def test_validation_rejects_before_launch():
     assert L.bsa_forward(fake, fake, fake, 0, ctypes.byref(g), fake, fake, None,
                          ctypes.c_float(float("inf")), fake, None, None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert L.bsa_status_string(2) == b"unsupported"
+    # clustering selector
+    for C, T in ((0, 3), (9, 3), (4, -1), (4, 17)):
+        assert L.bsa_cluster_importance(fake, 0, fake, ctypes.byref(g), C, T, 0, fake, None) == \
+            _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_cluster_importance(None, 0, fake, ctypes.byref(g), 4, 3, 0, fake, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_cluster_importance(fake, 0, fake, ctypes.byref(g), 4, 3, 0, mis, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    hy = _geo(W.workload("hunyuan_keep08").replace(k_block=16)).c()   # nkb 7441: 3 * 7441 > 16384
+    assert L.bsa_cluster_importance(fake, 0, fake, ctypes.byref(hy), 3, 3, 0, fake, None) == \
+        _lib.BSA_ERR_UNSUPPORTED
+    ps = _mp(w.replace(mode="sample")).c()
+    assert L.bsa_select_blocks(fake, ctypes.byref(g), ctypes.byref(ps), fake, fake, fake, None, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_select_blocks(None, ctypes.byref(g), ctypes.byref(p), fake, fake, fake, None, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
 
 
 def test_python_binding_raises_on_missing_gpu_tensors():
