@@ -24,6 +24,8 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attn fwd ms/call + effective TFLOP/s (frac of MFMA peak) at 90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# fp32 vector lane-ops without packed math: 256 CUs x 4 SIMDs x 16 lanes per clock at 2.4 GHz
+PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
 def _args():
@@ -35,6 +37,9 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-qblocks", type=int, default=512)
     ap.add_argument("--cpu-sample-heads", type=int, default=3)
+    ap.add_argument("--cluster-clusters", type=int, default=4,
+                    help="also time the intra-block clustering selector with this many clusters (0: skip)")
+    ap.add_argument("--cluster-iters", type=int, default=3)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -103,6 +108,46 @@ def cpu_baseline(w, q, k, v, nblocks, nheads):
             "seconds": round(wall, 2)}
 
 
+def cluster_selector_timing(bsa, w, g, p, qd, kp, C, T, nqb, nkb, stream, ev, reps=20):
+    """Intra-block clustering selector on the same inputs: importance, then selection.
+
+    Not part of the timed step.  VALU work per query block (lane-ops):
+    k-means (T+1) * n * C * D * 3 + T * n * C * D, logits C * nkb * D * 2;
+    the exponentials and the mixture are counted as C * nkb * 30.
+    """
+    import numpy as np
+    import torch
+    imp = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.float32, device=qd.device)
+    cnt = torch.empty((w.B, w.H, nqb), dtype=torch.int32, device=qd.device)
+    idx = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.int32, device=qd.device)
+    logw = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.float32, device=qd.device) if w.mode == "sample" else None
+    for _ in range(3):
+        bsa.bsa_cluster_importance(qd, kp, g, C, T, w.log_cluster, out=imp)
+        bsa.bsa_select_blocks(imp, g, p, want_mask=False, out=(None, cnt, idx, logw))
+    torch.cuda.synchronize()
+    ti, ts = [], []
+    for _ in range(reps):
+        e = [ev() for _ in range(3)]
+        e[0].record(stream)
+        bsa.bsa_cluster_importance(qd, kp, g, C, T, w.log_cluster, out=imp)
+        e[1].record(stream)
+        bsa.bsa_select_blocks(imp, g, p, want_mask=False, out=(None, cnt, idx, logw))
+        e[2].record(stream)
+        ti.append(e)
+    torch.cuda.synchronize()
+    imp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ti]))
+    sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ti]))
+    n = w.q_block
+    ops_row = (T + 1) * n * C * w.D * 3 + T * n * C * w.D + C * nkb * w.D * 2 + C * nkb * 30
+    lane_ops = float(w.B * w.H * nqb) * ops_row
+    tops = lane_ops / (imp_ms * 1e-3) / 1e12
+    return {"n_clusters": C, "iters": T, "importance_ms": round(imp_ms, 4), "select_ms": round(sel_ms, 4),
+            "executed_blocks": int(cnt.sum().item()),
+            "roofline": {"bound": "alu", "kernel": "importance_kernel", "achieved": round(tops, 2),
+                         "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s",
+                         "frac": round(tops / PEAK_VALU_TLANEOPS, 4)}}
+
+
 def main():
     a = _args()
     if a.calibrate_copy_mib:
@@ -116,7 +161,7 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU: the path has no multi-GPU part in this build "
+        print(f"bench.py runs on one GPU: the path has no multi-GPU part "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -219,6 +264,9 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
+    if a.cluster_clusters > 0 and a.cluster_clusters * nkb <= 16384:
+        res["cluster_selector"] = cluster_selector_timing(bsa, w, g, p, qd, kp, a.cluster_clusters,
+                                                          a.cluster_iters, nqb, nkb, stream, ev)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks, a.cpu_sample_heads)
     res["input_gen_s"] = round(t_gen, 1)

@@ -12,18 +12,20 @@
 //   1. the block's valid query tokens go to LDS as float32 (rows padded by
 //      one float, so a thread per token reads without bank conflicts);
 //   2. Lloyd k-means: centroid c starts at token floor(c n / C); each round
-//      assigns every token (one thread per token, squared distances as a
-//      sequential non-fused chain over the channels, the lowest cluster
+//      assigns every token (one thread per (token, cluster) distance, a
+//      sequential non-fused chain over the channels; the lowest cluster
 //      among equals) and replaces every non-empty centroid by the mean of
 //      its tokens (one thread per (cluster, channel), ascending tokens); a
 //      final assignment gives the cluster sizes;
-//   3. logits of every centroid against every key-block summary (one thread
-//      per key block, all centroids at once, the same chain as the block
-//      logits of the mask);
+//   3. logits of every centroid against every key-block summary (the same
+//      chain as the block logits of the mask), the summaries staged through
+//      LDS in chunks of 64 with coalesced loads, one thread per (key block,
+//      cluster);
 //   4. per non-empty cluster: row max, e = exp(z - max) by the fixed-order
 //      exponential, the sum by a halving tree over the row padded to a
-//      power of two, p = e / sum; the importance accumulates fl32(w p) with
-//      w = m_c / n, clusters in ascending order.
+//      power of two (levels of 64 and more through LDS, the rest by lane
+//      shuffles inside one wave, the same pairs), p = e / sum; the importance
+//      accumulates fl32(w p) with w = m_c / n, clusters in ascending order.
 // Every operation is a single float32 rounding in a fixed order, so the
 // importance (and the selection that ranks it) is reproducible bit for bit.
 #include "bsa_internal.h"
@@ -35,6 +37,7 @@ namespace {
 constexpr int kImpThreads = 256;
 constexpr int kMaxClusters = 8;
 constexpr int kMaxOwned = 32;   // key blocks per thread: nkb <= 8192
+constexpr int kChunk = 64;      // key-block summaries per LDS chunk
 
 template <typename T>
 __device__ __forceinline__ float widen(const T* p, int64_t e);
@@ -45,6 +48,12 @@ __device__ __forceinline__ float widen<bf16_t>(const bf16_t* p, int64_t e) {
 template <>
 __device__ __forceinline__ float widen<float>(const float* p, int64_t e) {
   return p[e];
+}
+
+// floats of the area that holds the tokens, then the key-block chunks
+__host__ __device__ inline int tok_floats(int q_block, int D) {
+  const int t = q_block * (D + 1), k = kChunk * (D + 4);
+  return t > k ? t : k;
 }
 
 template <typename T>
@@ -61,11 +70,12 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   const int n = (int)min((int64_t)a.q_block, a.S - lo);
   const int ce = min(a.C, n);
 
-  float* xs = lds;                                   // [q_block][D + 1]
-  float* mu = xs + a.q_block * DP;                   // [C][D]
+  float* xs = lds;                                   // [q_block][D + 1], later [kChunk][D + 4]
+  float* mu = xs + tok_floats(a.q_block, D);         // [C][D]
   int* asg = reinterpret_cast<int*>(mu + a.C * D);   // [q_block]
   int* msz = asg + a.q_block;                        // [8]
-  float* zb = reinterpret_cast<float*>(msz + kMaxClusters);   // [C][nkb]
+  float* dist = reinterpret_cast<float*>(msz + kMaxClusters); // [C][q_block]
+  float* zb = dist + a.C * a.q_block;                // [C][nkb]
   float* red = zb + a.C * nkb;                       // [max(256, P / 2)]
 
   // ---- 1. tokens ----
@@ -79,27 +89,29 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __syncthreads();
 
   // ---- 2. k-means ----
+  // distance of every (token, cluster) pair by its own thread, then the
+  // nearest cluster of every token (lowest index among equals)
   auto assign = [&]() {
-    for (int t = tid; t < n; t += kImpThreads) {
-      float acc[kMaxClusters];
-#pragma unroll
-      for (int c = 0; c < kMaxClusters; ++c) acc[c] = 0.0f;
+    for (int e = tid; e < n * ce; e += kImpThreads) {
+      const int t = e % n, c = e / n;
+      const float* xr = xs + t * DP;
+      const float* mr = mu + c * D;
+      float acc = 0.0f;
+#pragma unroll 8
       for (int d = 0; d < D; ++d) {
-        const float x = xs[t * DP + d];
-#pragma unroll
-        for (int c = 0; c < kMaxClusters; ++c) {
-          if (c < ce) {
-            const float df = __fsub_rn(x, mu[c * D + d]);
-            acc[c] = __fadd_rn(acc[c], __fmul_rn(df, df));
-          }
-        }
+        const float df = __fsub_rn(xr[d], mr[d]);
+        acc = __fadd_rn(acc, __fmul_rn(df, df));
       }
+      dist[e] = acc;
+    }
+    __syncthreads();
+    for (int t = tid; t < n; t += kImpThreads) {
       int best = 0;
-      float bd = acc[0];
-#pragma unroll
-      for (int c = 1; c < kMaxClusters; ++c) {
-        if (c < ce && acc[c] < bd) {
-          bd = acc[c];
+      float bd = dist[t];
+      for (int c = 1; c < ce; ++c) {
+        const float v = dist[c * n + t];
+        if (v < bd) {
+          bd = v;
           best = c;
         }
       }
@@ -111,13 +123,17 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     assign();
     for (int e = tid; e < ce * D; e += kImpThreads) {
       const int c = e / D, d = e % D;
+      // members in ascending token order; a non-member adds +0, which leaves
+      // a nonzero sum unchanged and can only turn a -0 sum into +0 (the same
+      // distances and logits: both enter through x - mu and mu * k, and a
+      // zero logit is stored as +0)
       float acc = 0.0f;
       int m = 0;
+#pragma unroll 8
       for (int t = 0; t < n; ++t) {
-        if (asg[t] == c) {
-          acc = __fadd_rn(acc, xs[t * DP + d]);
-          ++m;
-        }
+        const bool in = asg[t] == c;
+        acc = __fadd_rn(acc, in ? xs[t * DP + d] : 0.0f);
+        m += in ? 1 : 0;
       }
       if (m > 0) mu[e] = __fdiv_rn(acc, (float)m);
     }
@@ -132,36 +148,42 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __syncthreads();
 
   // ---- 3. logits of every centroid against every key-block summary ----
+  // The summaries go through LDS (the token area, free by now) in chunks of
+  // kChunk rows with coalesced loads; one thread per (row of the chunk,
+  // cluster), threads of a wave on consecutive rows of one cluster.
   const float* kb = a.kp + (int64_t)bh * nkb * D;
-  for (int j = tid; j < nkb; j += kImpThreads) {
-    float acc[kMaxClusters];
-#pragma unroll
-    for (int c = 0; c < kMaxClusters; ++c) acc[c] = 0.0f;
-    const float* kr = kb + (int64_t)j * D;
-    for (int d = 0; d < D; d += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
-#pragma unroll
-      for (int c = 0; c < kMaxClusters; ++c) {
-        if (c < ce) {
-          const float* m = mu + c * D + d;
-          float t = acc[c];
-          t = __fadd_rn(t, __fmul_rn(m[0], kv.x));
-          t = __fadd_rn(t, __fmul_rn(m[1], kv.y));
-          t = __fadd_rn(t, __fmul_rn(m[2], kv.z));
-          t = __fadd_rn(t, __fmul_rn(m[3], kv.w));
-          acc[c] = t;
-        }
-      }
+  const int KS = D + 4;                              // padded row stride (16-byte rows)
+  float* ks = xs;
+  for (int j0 = 0; j0 < nkb; j0 += kChunk) {
+    const int nj = min(kChunk, nkb - j0);
+    __syncthreads();                                 // the previous chunk is consumed
+    const int D4 = D / 4;
+    for (int e = tid; e < nj * D4; e += kImpThreads) {
+      const int r = e / D4, c4 = e % D4;
+      *reinterpret_cast<float4*>(ks + r * KS + 4 * c4) =
+          *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + r) * D + 4 * c4);
     }
-    const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
-#pragma unroll
-    for (int c = 0; c < kMaxClusters; ++c) {
-      if (c < ce) {
-        float z = __fmul_rn(acc[c], a.scale);
-        if (a.log_cluster) z = __fadd_rn(z, lc);
-        if (z == 0.0f) z = 0.0f;                    // -0 -> +0
-        zb[c * nkb + j] = z;
+    __syncthreads();
+    for (int e = tid; e < kChunk * ce; e += kImpThreads) {
+      const int jl = e % kChunk, c = e / kChunk;
+      if (jl >= nj) continue;
+      const float* kr = ks + jl * KS;
+      const float* mr = mu + c * D;
+      float acc = 0.0f;
+      for (int d = 0; d < D; d += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(kr + d);
+        const float4 m = *reinterpret_cast<const float4*>(mr + d);
+        acc = __fadd_rn(acc, __fmul_rn(m.x, kv.x));
+        acc = __fadd_rn(acc, __fmul_rn(m.y, kv.y));
+        acc = __fadd_rn(acc, __fmul_rn(m.z, kv.z));
+        acc = __fadd_rn(acc, __fmul_rn(m.w, kv.w));
       }
+      const int j = j0 + jl;
+      const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
+      float z = __fmul_rn(acc, a.scale);
+      if (a.log_cluster) z = __fadd_rn(z, lc);
+      if (z == 0.0f) z = 0.0f;                      // -0 -> +0
+      zb[c * nkb + j] = z;
     }
   }
   __syncthreads();
@@ -177,13 +199,11 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     float* zc = zb + c * nkb;
     float m = -INFINITY;
     for (int j = tid; j < nkb; j += kImpThreads) m = fmaxf(m, zc[j]);
-    red[tid] = m;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
-    for (int s = kImpThreads / 2; s > 0; s >>= 1) {
-      if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-      __syncthreads();
-    }
-    const float M = red[0];
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));   // max is exact in any order
     __syncthreads();
     for (int j = tid; j < nkb; j += kImpThreads) zc[j] = exp_le0(__fsub_rn(zc[j], M));
     __syncthreads();
@@ -198,10 +218,25 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
         red[k] = __fadd_rn(v0, v1);
       }
       __syncthreads();
-      for (int h = h0 / 2; h >= 1; h >>= 1) {
+      // halving levels across waves through LDS while more than 64 values
+      // remain, the rest inside wave 0 with the same pairs (lane k adds lane
+      // k + h)
+      int cnt = h0;
+      for (; cnt > 64; cnt >>= 1) {
+        const int h = cnt >> 1;
         for (int k = tid; k < h; k += kImpThreads) red[k] = __fadd_rn(red[k], red[k + h]);
         __syncthreads();
       }
+      if (tid < 64) {
+        float v = tid < cnt ? red[tid] : 0.0f;
+        for (; cnt > 1; cnt >>= 1) {
+          const int h = cnt >> 1;
+          const float o = __shfl_down(v, h, 64);
+          if (tid < h) v = __fadd_rn(v, o);
+        }
+        if (tid == 0) red[0] = v;
+      }
+      __syncthreads();
       Z = red[0];
     }
     const float w = __fdiv_rn((float)msz[c], (float)n);
@@ -226,8 +261,8 @@ size_t importance_lds_bytes(const ImpArgs& a) {
   int P = 1;
   while (P < a.nkb) P <<= 1;
   const size_t red = (size_t)(P / 2 > kImpThreads ? P / 2 : kImpThreads);
-  return sizeof(float) * ((size_t)a.q_block * (a.D + 1) + (size_t)a.C * a.D + (size_t)a.q_block +
-                          kMaxClusters + (size_t)a.C * a.nkb + red);
+  return sizeof(float) * ((size_t)tok_floats(a.q_block, a.D) + (size_t)a.C * a.D + (size_t)a.q_block +
+                          kMaxClusters + (size_t)a.C * a.q_block + (size_t)a.C * a.nkb + red);
 }
 
 hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream) {
