@@ -27,7 +27,7 @@ from ._lib import BsaError
 
 __all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
            "bsa_build_mask", "bsa_forward", "bsa_cluster_importance", "bsa_select_blocks",
-           "library_path"]
+           "bsa_select_top_p", "DOMAINS", "library_path"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -202,6 +202,38 @@ def bsa_select_blocks(importance: torch.Tensor, g: Geometry, p: MaskParams, want
     _lib.check(_lib.lib().bsa_select_blocks(_ptr(importance), ctypes.byref(g.c()), ctypes.byref(p.c()),
                                             _ptr(mask), _ptr(cnt), _ptr(idx), _ptr(logw), _stream(stream)))
     return mask, cnt, idx, logw
+
+
+DOMAINS = {"row": 0, "head": 1, "split": 2, "all": 3, "eg": 4}
+
+
+def bsa_select_top_p(scores: torch.Tensor, g: Geometry, domain: str = "eg", top_p: float = 0.9,
+                     v_pooled: Optional[torch.Tensor] = None, value_aware: bool = False,
+                     entropy_eps: float = 1e-12, frame0_dense: bool = False, text_columns: bool = False,
+                     workspace: Optional[torch.Tensor] = None, want_mask: bool = True, stream=None):
+    """Top-p over competition domains -> (mask u8 or None, kv_cnt, kv_idx, head entropy f64 [B,H])."""
+    d = bsa_derive(g)
+    nqb, nkb = d["nqb"], d["nkb"]
+    dev = scores.device
+    _need(scores, "scores", (g.B, g.H, nqb, nkb), torch.float32)
+    if value_aware:
+        _need(v_pooled, "v_pooled", (g.B, g.H, nkb, g.head_dim), torch.float32, dev)
+    nbytes = ctypes.c_int64()
+    _lib.check(_lib.lib().bsa_top_p_workspace_bytes(ctypes.byref(g.c()), ctypes.byref(nbytes)))
+    if workspace is None:
+        workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    mask = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
+    cnt = torch.empty((g.B, g.H, nqb), dtype=torch.int32, device=dev)
+    idx = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.int32, device=dev)
+    ent = torch.empty((g.B, g.H), dtype=torch.float64, device=dev)
+    tp = _lib.bsa_topp_params(DOMAINS[domain], 1 if value_aware else 0, float(top_p), float(entropy_eps),
+                              1 if frame0_dense else 0, 1 if text_columns else 0, 0)
+    _lib.check(_lib.lib().bsa_select_top_p(_ptr(scores), _ptr(v_pooled) if value_aware else None,
+                                           ctypes.byref(g.c()), ctypes.byref(tp), _ptr(ent), _ptr(workspace),
+                                           workspace.numel(), _ptr(mask), _ptr(cnt), _ptr(idx),
+                                           _stream(stream)))
+    return mask, cnt, idx, ent
 
 
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,

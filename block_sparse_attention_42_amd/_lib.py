@@ -15,7 +15,7 @@ BSA_SELECT_TOPK = 0
 BSA_SELECT_SAMPLE = 1
 
 EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward",
-            "bsa_cluster_importance", "bsa_select_blocks",
+            "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes", "bsa_select_top_p",
             "bsa_status_string", "bsa_last_error", "bsa_abi_version"]
 
 
@@ -33,6 +33,13 @@ class bsa_mask_params(ctypes.Structure):
                 ("keep_ratio", ctypes.c_double), ("frame0_dense", ctypes.c_int32),
                 ("text_columns", ctypes.c_int32), ("log_cluster", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class bsa_topp_params(ctypes.Structure):
+    _fields_ = [("domain", ctypes.c_int32), ("value_aware", ctypes.c_int32),
+                ("top_p", ctypes.c_double), ("entropy_eps", ctypes.c_float),
+                ("frame0_dense", ctypes.c_int32), ("text_columns", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class bsa_derived(ctypes.Structure):
@@ -63,8 +70,12 @@ def lib():
         L.bsa_cluster_importance.argtypes = [P, ctypes.c_int32, P, G, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, P, P]
         L.bsa_select_blocks.argtypes = [P, G, M, P, P, P, P, P]
+        L.bsa_top_p_workspace_bytes.argtypes = [G, ctypes.POINTER(ctypes.c_int64)]
+        L.bsa_select_top_p.argtypes = [P, P, G, ctypes.POINTER(bsa_topp_params), P, P, ctypes.c_int64,
+                                       P, P, P, P]
         for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_abi_version",
-                  "bsa_cluster_importance", "bsa_select_blocks"):
+                  "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes",
+                  "bsa_select_top_p"):
             getattr(L, f).restype = ctypes.c_int32
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p

@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libbsa.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "forward.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "topp.hip", "forward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are switched off for every device pass.
@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # Pooling and mask decisions follow a written-out float32 operation order:
 # no contraction into fused multiply-adds anywhere in those files.
 EXTRA = {"pool.hip": ["-ffp-contract=off"], "mask.hip": ["-ffp-contract=off"],
-         "cluster.hip": ["-ffp-contract=off"],
+         "cluster.hip": ["-ffp-contract=off"], "topp.hip": ["-ffp-contract=off"],
          "abi.cpp": ["-x", "hip", "-ffp-contract=off"]}
 
 

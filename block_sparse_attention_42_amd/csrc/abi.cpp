@@ -300,6 +300,72 @@ bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g, con
   return ok();
 }
 
+bsa_status bsa_top_p_workspace_bytes(const bsa_geometry* g, int64_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  *bytes = bsa::topp_workspace_bytes((int64_t)g->B * g->H, g->B, d.nqb, d.nkb);
+  return ok();
+}
+
+bsa_status bsa_select_top_p(const float* scores, const float* v_pooled, const bsa_geometry* g,
+                            const bsa_topp_params* tp, double* head_entropy, void* workspace,
+                            int64_t workspace_bytes, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx,
+                            void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (!tp) return fail(BSA_ERR_INVALID_ARGUMENT, "top-p params are NULL");
+  if (tp->domain < BSA_DOMAIN_ROW || tp->domain > BSA_DOMAIN_EG)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown domain %d", tp->domain);
+  if (!(std::isfinite(tp->top_p) && tp->top_p > 0.0 && tp->top_p <= 1.0))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "top_p %g must be in (0, 1]", tp->top_p);
+  if (!(std::isfinite(tp->entropy_eps) && tp->entropy_eps > 0.0f))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "entropy_eps must be finite and > 0");
+  if (!scores || !workspace || !kv_cnt || !kv_idx)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "scores, workspace, kv_cnt and kv_idx must not be NULL");
+  if (tp->value_aware && !v_pooled) return fail(BSA_ERR_INVALID_ARGUMENT, "value-aware scores need v_pooled");
+  if (!aligned16(scores) || !aligned16(workspace) || !aligned16(kv_cnt) || !aligned16(kv_idx) ||
+      (mask && !aligned16(mask)) || (head_entropy && !aligned16(head_entropy)) ||
+      (tp->value_aware && !aligned16(v_pooled)))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (d.nkb > 2048) return fail(BSA_ERR_UNSUPPORTED, "nkb %d > 2048 for top-p selection", d.nkb);
+  if (g->H > 4096) return fail(BSA_ERR_UNSUPPORTED, "H %d > 4096 for top-p selection", g->H);
+  if ((int64_t)g->B * g->H * d.nqb > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+  const int64_t need = bsa::topp_workspace_bytes((int64_t)g->B * g->H, g->B, d.nqb, d.nkb);
+  if (workspace_bytes < need)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "workspace of %lld bytes < %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  bsa::TopPArgs a = {};
+  a.scores = scores;
+  a.vp = tp->value_aware ? v_pooled : nullptr;
+  a.ws = workspace;
+  a.entropy_out = head_entropy;
+  a.mask = mask;
+  a.cnt = kv_cnt;
+  a.idx = kv_idx;
+  a.B = g->B;
+  a.H = g->H;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.D = g->head_dim;
+  a.vstride = (d.nkb + 3) / 4 * 4;
+  a.npools = a.BH > 2 * g->B ? a.BH : 2 * g->B;
+  a.domain = tp->domain;
+  a.value_aware = tp->value_aware ? 1 : 0;
+  a.top_p = tp->top_p;
+  a.eps = tp->entropy_eps;
+  a.frame0_first = tp->frame0_dense ? d.f0_first : -1;
+  a.frame0_last = tp->frame0_dense ? d.f0_last : -1;
+  a.text_last = tp->text_columns ? d.text_last : -1;
+  hipError_t e = bsa::launch_topp(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "top-p launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtype,
                        const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
                        const float* log_w, float softmax_scale, void* out, float* lse,

@@ -44,6 +44,26 @@ struct MaskArgs {
   const float* imp;   // [BH, nqb, nkb] block importance to select from (qp, kp unused), or null
 };
 
+// Launch arguments of the top-p / competition-domain selection kernels.
+struct TopPArgs {
+  const float* scores;   // [BH, nqb, nkb] P' (>= 0)
+  const float* vp;       // [BH, nkb, D] pooled values (value-aware scores) or null
+  void* ws;              // workspace (topp_workspace_bytes)
+  double* entropy_out;   // [BH] or null
+  uint8_t* mask;         // [BH, nqb, nkb] or null
+  int32_t* cnt;          // [BH, nqb]
+  int32_t* idx;          // [BH, nqb, nkb]
+  int32_t B, H, BH, nqb, nkb, D;
+  int32_t vstride;       // row stride of the value norms in the workspace
+  int32_t npools;
+  int32_t domain;        // 0 row, 1 head, 2 split, 3 all, 4 EG-Sparse routing
+  int32_t value_aware;
+  double top_p;
+  float eps;
+  int32_t frame0_first, frame0_last;   // -1 if off
+  int32_t text_last;                   // -1 if off
+};
+
 // Launch arguments of the block-importance kernel (intra-block clusters).
 struct ImpArgs {
   const void* q;      // [BH, seq_alloc, D]
@@ -91,6 +111,8 @@ inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 size_t importance_lds_bytes(const ImpArgs& a);
+int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb);
+hipError_t launch_topp(const TopPArgs& a, hipStream_t stream);
 hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 

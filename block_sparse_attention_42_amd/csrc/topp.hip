@@ -1,0 +1,360 @@
+// Top-p selection over competition domains on gfx950.
+//
+// Page: "Competition Domains Matter ... (EG-Sparse)": per-head attention
+// entropy (its Eq. 3); the domain hierarchy of its Section 3.3 (per-row
+// local, per-head global, grouped cross-head split at the entropy median,
+// all-head global) and its deployed routing (low-entropy heads share one
+// pool, the others stay per-row local); top-p of a domain's score mass; the
+// value-aware score of the cross-head pool (P' times the norm of the key
+// cluster's value centroid); the one-key-per-row safeguard.
+//
+// Mass is counted in fixed point, m(s) = floor(s * 2^32) + 1, so a pool's
+// mass is an exact integer whatever the summation order, and its threshold
+// -- the largest score T with mass(score >= T) >= ceil(p * mass(pool)) --
+// is found by a radix select over the scores' order keys with integer bin
+// masses (four 8-bit passes, integer atomics).  A per-row local domain finds
+// its T by a bitwise search inside one wave.  Every block with score >= T is
+// kept.
+//
+// Kernels, in launch order (grid-wide dependencies between them):
+//   tp_row_entropy  one workgroup per row: sum_j -P log(P + eps) (float64)
+//   tp_heads        one workgroup per batch element: head entropies, median
+//                   split, pool of every head, pool state cleared
+//   tp_value_norm   norm of every pooled value row (value-aware scores)
+//   tp_total        one workgroup per pooled row: its mass into the pool total
+//   tp_target       per pool: target = ceil(p * total)
+//   tp_hist, tp_digit (x4)  radix passes of the pooled thresholds
+//   tp_select       one wave per row: threshold (pool's, or its own search),
+//                   safeguard, frame-0 rows, text columns, compaction
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kTpThreads = 256;
+constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks in registers
+
+struct PoolState {
+  unsigned long long total, target, rem;
+  uint32_t prefix, used;
+  unsigned long long bins[256];
+};
+
+__device__ __forceinline__ uint32_t okey(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long fixed_mass(float s) {
+  return (unsigned long long)floor((double)s * 4294967296.0) + 1ull;
+}
+
+struct Ws {
+  double* row_ent;        // [BH * nqb]
+  double* head_ent;       // [BH]
+  int32_t* pool;          // [BH]
+  float* vnorm;           // [BH * nkb]
+  PoolState* ps;          // [npools]
+};
+
+__device__ __forceinline__ Ws ws_of(const TopPArgs& a) {
+  char* p = reinterpret_cast<char*>(a.ws);
+  Ws w;
+  w.row_ent = reinterpret_cast<double*>(p);
+  p += sizeof(double) * (size_t)a.BH * a.nqb;
+  w.head_ent = reinterpret_cast<double*>(p);
+  p += sizeof(double) * (size_t)a.BH;
+  w.pool = reinterpret_cast<int32_t*>(p);
+  p += sizeof(int32_t) * (size_t)((a.BH + 1) / 2 * 2);
+  w.vnorm = reinterpret_cast<float*>(p);
+  p += sizeof(float) * (size_t)a.BH * ((a.nkb + 3) / 4 * 4);
+  w.ps = reinterpret_cast<PoolState*>(p);
+  return w;
+}
+
+// the ranking score of block j of a row of head bh
+__device__ __forceinline__ float score_of(const TopPArgs& a, const Ws& w, int bh, int64_t row, int j, bool pooled) {
+  const float s = a.scores[row * a.nkb + j];
+  return (a.value_aware && pooled) ? __fmul_rn(s, w.vnorm[(int64_t)bh * a.vstride + j]) : s;
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a) {
+  __shared__ double red[kTpThreads];
+  const Ws w = ws_of(a);
+  const int64_t row = blockIdx.x;
+  const float* s = a.scores + row * a.nkb;
+  const double eps = (double)a.eps;
+  double acc = 0.0;
+  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
+    const double p = (double)s[j];
+    acc -= p * log(p + eps);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = kTpThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) w.row_ent[row] = red[0];
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_heads(TopPArgs a) {
+  extern __shared__ double hent[];          // [H]
+  const Ws w = ws_of(a);
+  const int b = blockIdx.x;
+  const int H = a.H;
+  for (int h = threadIdx.x; h < H; h += kTpThreads) {
+    double acc = 0.0;
+    const double* r = w.row_ent + ((int64_t)b * H + h) * a.nqb;
+    for (int i = 0; i < a.nqb; ++i) acc += r[i];
+    hent[h] = acc / (double)a.nqb;
+  }
+  __syncthreads();
+  for (int h = threadIdx.x; h < H; h += kTpThreads) {
+    int rank = 0;
+    for (int o = 0; o < H; ++o) rank += (hent[o] < hent[h] || (hent[o] == hent[h] && o < h)) ? 1 : 0;
+    const bool low = rank < H / 2;
+    int pid;
+    switch (a.domain) {
+      case 1: pid = b * H + h; break;                          // per-head global
+      case 2: pid = 2 * b + (low ? 0 : 1); break;              // grouped cross-head
+      case 3: pid = b; break;                                  // all-head global
+      case 4: pid = low ? b : -1; break;                       // EG-Sparse routing
+      default: pid = -1; break;                                // per-row local
+    }
+    w.pool[b * H + h] = pid;
+    w.head_ent[b * H + h] = hent[h];
+    if (a.entropy_out) a.entropy_out[b * H + h] = hent[h];
+  }
+  // clear the state of this batch element's pools
+  int lo, hi;
+  switch (a.domain) {
+    case 1: lo = b * H; hi = b * H + H; break;
+    case 2: lo = 2 * b; hi = 2 * b + 2; break;
+    case 3: case 4: lo = b; hi = b + 1; break;
+    default: lo = hi = 0; break;
+  }
+  for (int q = lo; q < hi; ++q) {
+    PoolState* ps = w.ps + q;
+    for (int d = threadIdx.x; d < 256; d += kTpThreads) ps->bins[d] = 0ull;
+    if (threadIdx.x == 0) {
+      ps->total = 0ull;
+      ps->target = 0ull;
+      ps->rem = 0ull;
+      ps->prefix = 0u;
+      ps->used = 0u;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_value_norm(TopPArgs a) {
+  const Ws w = ws_of(a);
+  const int64_t e = (int64_t)blockIdx.x * kTpThreads + threadIdx.x;   // bh * nkb + j
+  if (e >= (int64_t)a.BH * a.nkb) return;
+  const int bh = (int)(e / a.nkb), j = (int)(e % a.nkb);
+  const float* v = a.vp + e * a.D;
+  float acc = 0.0f;
+  for (int d = 0; d < a.D; ++d) acc = __fadd_rn(acc, __fmul_rn(v[d], v[d]));
+  w.vnorm[(int64_t)bh * a.vstride + j] = __fsqrt_rn(acc);
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_total(TopPArgs a) {
+  __shared__ unsigned long long red[kTpThreads];
+  const Ws w = ws_of(a);
+  const int64_t row = blockIdx.x;
+  const int bh = (int)(row / a.nqb);
+  const int pid = w.pool[bh];
+  if (pid < 0) return;                                       // uniform over the workgroup
+  unsigned long long acc = 0ull;
+  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) acc += fixed_mass(score_of(a, w, bh, row, j, true));
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = kTpThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    atomicAdd(&w.ps[pid].total, red[0]);
+    w.ps[pid].used = 1u;
+  }
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_target(TopPArgs a) {
+  const Ws w = ws_of(a);
+  for (int q = threadIdx.x; q < a.npools; q += kTpThreads) {
+    PoolState* ps = w.ps + q;
+    if (!ps->used) continue;
+    ps->target = (unsigned long long)ceil(a.top_p * (double)ps->total);
+    ps->rem = ps->target;
+    ps->prefix = 0u;
+  }
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
+  __shared__ unsigned long long bins[256];
+  const Ws w = ws_of(a);
+  const int64_t row = blockIdx.x;
+  const int bh = (int)(row / a.nqb);
+  const int pid = w.pool[bh];
+  if (pid < 0) return;
+  bins[threadIdx.x] = 0ull;
+  __syncthreads();
+  const uint32_t prefix = w.ps[pid].prefix;
+  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
+    const float s = score_of(a, w, bh, row, j, true);
+    const uint32_t k = okey(s);
+    const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u;
+    if (match) atomicAdd(&bins[(k >> shift) & 255u], fixed_mass(s));
+  }
+  __syncthreads();
+  const unsigned long long v = bins[threadIdx.x];
+  if (v) atomicAdd(&w.ps[pid].bins[threadIdx.x], v);
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
+  const Ws w = ws_of(a);
+  for (int q = threadIdx.x; q < a.npools; q += kTpThreads) {
+    PoolState* ps = w.ps + q;
+    if (!ps->used) continue;
+    unsigned long long acc = 0ull;
+    int digit = 0;
+    for (int d = 255; d >= 0; --d) {
+      const unsigned long long bd = ps->bins[d];
+      if (acc + bd >= ps->rem) {
+        digit = d;
+        ps->rem -= acc;                                     // mass of larger digits in the group
+        break;
+      }
+      acc += bd;
+    }
+    ps->prefix |= (uint32_t)digit << shift;
+    for (int d = 0; d < 256; ++d) ps->bins[d] = 0ull;
+  }
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
+  const Ws w = ws_of(a);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
+  const int bh = (int)(row / a.nqb);
+  const int i = (int)(row % a.nqb);
+  const int n = a.nkb;
+  const int pid = w.pool[bh];
+  const bool pooled = pid >= 0;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint8_t* mrow = a.mask ? a.mask + row * n : nullptr;
+  int32_t* irow = a.idx + row * n;
+  const bool dense = a.frame0_first >= 0 && i >= a.frame0_first && i <= a.frame0_last;
+
+  float sc[kTpPerLane];
+  uint32_t key[kTpPerLane];
+#pragma unroll
+  for (int mm = 0; mm < kTpPerLane; ++mm) {
+    const int j = lane + 64 * mm;
+    sc[mm] = j < n ? score_of(a, w, bh, row, j, pooled) : 0.0f;
+    key[mm] = j < n ? okey(sc[mm]) : 0u;                     // 0: below every score's key
+  }
+  uint32_t T;
+  if (pooled) {
+    T = w.ps[pid].prefix;
+  } else {
+    unsigned long long tot = 0ull;
+#pragma unroll
+    for (int mm = 0; mm < kTpPerLane; ++mm)
+      if (lane + 64 * mm < n) tot += fixed_mass(sc[mm]);
+    tot = wave_sum_u64(tot);
+    const unsigned long long target = (unsigned long long)ceil(a.top_p * (double)tot);
+    T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      unsigned long long m = 0ull;
+#pragma unroll
+      for (int mm = 0; mm < kTpPerLane; ++mm)
+        if (key[mm] >= cand) m += fixed_mass(sc[mm]);
+      m = wave_sum_u64(m);
+      if (m >= target) T = cand;
+    }
+  }
+  // kept: score >= T; a pooled row left empty keeps its first largest block
+  bool any = false;
+#pragma unroll
+  for (int mm = 0; mm < kTpPerLane; ++mm) any = any || (lane + 64 * mm < n && key[mm] >= T);
+  const bool row_empty = !__any(any);
+  int safe = -1;
+  if (pooled && row_empty) {
+    float best = -1.0f;
+    int bj = n;
+#pragma unroll
+    for (int mm = 0; mm < kTpPerLane; ++mm) {
+      const int j = lane + 64 * mm;
+      if (j < n && (sc[mm] > best || (sc[mm] == best && j < bj))) {
+        best = sc[mm];
+        bj = j;
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float ob = __shfl_xor(best, s, 64);
+      const int oj = __shfl_xor(bj, s, 64);
+      if (ob > best || (ob == best && oj < bj)) {
+        best = ob;
+        bj = oj;
+      }
+    }
+    safe = bj;
+  }
+  int run = 0;
+#pragma unroll
+  for (int mm = 0; mm < kTpPerLane; ++mm) {
+    const int j = lane + 64 * mm;
+    if (64 * mm >= n) break;
+    const bool in = j < n;
+    bool sel = in && (dense || key[mm] >= T || j == safe || j <= a.text_last);
+    const uint64_t bsel = __ballot(sel);
+    const int pos = run + __popcll(bsel & below);
+    if (in && mrow) mrow[j] = sel ? 1 : 0;
+    if (sel) irow[pos] = j;
+    run += __popcll(bsel);
+  }
+  if (lane == 0) a.cnt[row] = run;
+}
+
+}  // namespace
+
+int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb) {
+  const int64_t npools = BH > 2 * B ? BH : 2 * B;
+  return (int64_t)sizeof(double) * BH * nqb + (int64_t)sizeof(double) * BH +
+         (int64_t)sizeof(int32_t) * ((BH + 1) / 2 * 2) + (int64_t)sizeof(float) * BH * ((nkb + 3) / 4 * 4) +
+         (int64_t)sizeof(PoolState) * npools;
+}
+
+hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
+  const unsigned rows = (unsigned)((int64_t)a.BH * a.nqb);
+  hipLaunchKernelGGL(tp_row_entropy, dim3(rows), dim3(kTpThreads), 0, stream, a);
+  hipLaunchKernelGGL(tp_heads, dim3((unsigned)a.B), dim3(kTpThreads), sizeof(double) * a.H, stream, a);
+  if (a.value_aware) {
+    const int64_t n = (int64_t)a.BH * a.nkb;
+    hipLaunchKernelGGL(tp_value_norm, dim3((unsigned)((n + kTpThreads - 1) / kTpThreads)), dim3(kTpThreads), 0,
+                       stream, a);
+  }
+  if (a.domain != 0) {
+    hipLaunchKernelGGL(tp_total, dim3(rows), dim3(kTpThreads), 0, stream, a);
+    hipLaunchKernelGGL(tp_target, dim3(1), dim3(kTpThreads), 0, stream, a);
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hipLaunchKernelGGL(tp_hist, dim3(rows), dim3(kTpThreads), 0, stream, a, shift);
+      hipLaunchKernelGGL(tp_digit, dim3(1), dim3(kTpThreads), 0, stream, a, shift);
+    }
+  }
+  const unsigned groups = (unsigned)(((int64_t)a.BH * a.nqb + 3) / 4);
+  hipLaunchKernelGGL(tp_select, dim3(groups), dim3(kTpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -14,7 +14,8 @@
  *      an optional additive per-block log-weight  (bsa_forward);
  *   and, as a finer selector, block importance from k-means representatives
  *   of each query block (bsa_cluster_importance) with selection from any
- *   importance matrix (bsa_select_blocks).
+ *   importance matrix (bsa_select_blocks); and top-p selection over
+ *   competition domains routed by per-head entropy (bsa_select_top_p).
  *
  * Pages followed (title; section):
  *   - "Attention matrix view: make only frame-0 query rows dense": sec. 1
@@ -227,6 +228,53 @@ bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_p
 bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g,
                              const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
                              int32_t* kv_idx, float* log_w, void* stream);
+
+/* Top-p selection over competition domains (EG-Sparse page: per-head
+ * entropy, Eq. 3; the domain hierarchy of its Section 3.3; its deployed
+ * routing of low-entropy heads to a shared pool; the value-aware score of
+ * the cross-head pool; the one-key-per-row safeguard). */
+typedef enum {
+  BSA_DOMAIN_ROW = 0,    /* per-row local: each row keeps its own top-p */
+  BSA_DOMAIN_HEAD = 1,   /* per-head global: all rows of a head share one pool */
+  BSA_DOMAIN_SPLIT = 2,  /* grouped cross-head: low- and high-entropy heads, two pools */
+  BSA_DOMAIN_ALL = 3,    /* all-head global: one pool per batch element */
+  BSA_DOMAIN_EG = 4      /* low-entropy heads share a pool, the others per-row local */
+} bsa_domain;
+
+typedef struct {
+  int32_t domain;        /* bsa_domain */
+  int32_t value_aware;   /* pooled domains rank by fl32(P' * ||v̄_j||) (needs v_pooled) */
+  double top_p;          /* in (0, 1] */
+  float entropy_eps;     /* > 0: H_h = (1/nqb) sum_i sum_j -P' ln(P' + eps) */
+  int32_t frame0_dense;  /* query blocks overlapping frame 0 keep every block */
+  int32_t text_columns;  /* every row keeps the key blocks overlapping the text */
+  int32_t reserved;
+} bsa_topp_params;
+
+/* Bytes of device workspace bsa_select_top_p needs for this geometry. */
+bsa_status bsa_top_p_workspace_bytes(const bsa_geometry* g, int64_t* bytes);
+
+/*   scores:      [B, H, nqb, nkb] float32 P' (finite, >= 0, each row of mass
+ *                about 1; e.g. bsa_cluster_importance with one cluster).
+ *   v_pooled:    [B, H, nkb, D] float32 (bsa_pool_blocks of V with k_block)
+ *                when value_aware, else ignored (may be NULL).
+ *   head_entropy: [B, H] float64 written, or NULL.
+ *   workspace:   device buffer of at least bsa_top_p_workspace_bytes bytes,
+ *                owned by the caller, overwritten; calls that share one
+ *                workspace must not overlap.
+ *   mask, kv_cnt, kv_idx: as for bsa_build_mask.
+ * Mass is counted in fixed point, m(s) = floor(s * 2^32) + 1, exact in any
+ * order; a domain keeps every block whose score is at least T, the largest
+ * score with mass(score >= T) >= ceil(top_p * mass(domain)).  The median
+ * split puts the floor(H/2) lowest-entropy heads of each batch element
+ * (lower head first among equals) in the low group.  In a pooled domain a
+ * row left empty keeps its first block of largest score.  Frame-0 rows and
+ * text columns are applied after.  Limits: nkb <= 2048 (BSA_ERR_UNSUPPORTED
+ * beyond); pooled value-aware scores should stay below 2^16. */
+bsa_status bsa_select_top_p(const float* scores, const float* v_pooled, const bsa_geometry* g,
+                            const bsa_topp_params* tp, double* head_entropy, void* workspace,
+                            int64_t workspace_bytes, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx,
+                            void* stream);
 
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);

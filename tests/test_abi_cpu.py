@@ -122,6 +122,29 @@ def test_validation_rejects_before_launch():
         _lib.BSA_ERR_INVALID_ARGUMENT
     assert L.bsa_select_blocks(None, ctypes.byref(g), ctypes.byref(p), fake, fake, fake, None, None) == \
         _lib.BSA_ERR_INVALID_ARGUMENT
+    # top-p over competition domains
+    nb = ctypes.c_int64()
+    assert L.bsa_top_p_workspace_bytes(ctypes.byref(g), ctypes.byref(nb)) == _lib.BSA_OK and nb.value > 0
+
+    def tp(**kw):
+        base = dict(domain=4, value_aware=0, top_p=0.9, entropy_eps=1e-12, frame0_dense=0, text_columns=0,
+                    reserved=0)
+        base.update(kw)
+        return _lib.bsa_topp_params(**base)
+
+    def sel(t, vp=None, ws_bytes=None, geo=g):
+        return L.bsa_select_top_p(fake, vp, ctypes.byref(geo), ctypes.byref(t), None, fake,
+                                  nb.value if ws_bytes is None else ws_bytes, fake, fake, fake, None)
+    for bad in (tp(domain=5), tp(domain=-1), tp(top_p=0.0), tp(top_p=1.5), tp(entropy_eps=0.0),
+                tp(value_aware=1)):
+        assert sel(bad) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert sel(tp(), ws_bytes=nb.value - 8) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert b"workspace" in L.bsa_last_error()
+    big = _geo(W.workload("wan_1p3b_sampled_k16")).c()                  # nkb 2048: allowed
+    assert L.bsa_top_p_workspace_bytes(ctypes.byref(big), ctypes.byref(nb)) == _lib.BSA_OK
+    bigger = _geo(W.workload("hunyuan_keep08").replace(k_block=32)).c()   # nkb 3721 > 2048
+    L.bsa_top_p_workspace_bytes(ctypes.byref(bigger), ctypes.byref(nb))
+    assert sel(tp(), geo=bigger) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def test_python_binding_raises_on_missing_gpu_tensors():

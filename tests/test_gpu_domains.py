@@ -1,0 +1,130 @@
+"""GPU parity of top-p selection over competition domains through the C ABI.
+
+The scores are the GPU's P' (bsa_cluster_importance with one cluster, itself
+bit-exact against the oracle).  Bit-exact: masks, counts and lists for every
+domain, with and without value-aware pooled scores.  Head entropies within
+1e-9 relative (float64, the hardware log), and the test inputs keep the
+median split unambiguous, so both sides route the same heads.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.domains as dm
+import workloads as W
+from helpers import geometry_of, inputs_of, tiny
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+bsa = pytest.importorskip("block_sparse_attention_42_amd")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _geo(w):
+    return bsa.Geometry(w.B, w.H, w.text_len, w.frames, w.latent_h, w.latent_w, w.D,
+                        w.q_block, w.k_block, w.seq_alloc)
+
+
+def _dev(w, a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if w.dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+W_SMALL = tiny(text_len=40, frames=4, lh=10, lw=14, bq=64, bk=16, D=128, H=6, dtype="bf16", mode="topk",
+               topk=0, keep_ratio=0.2, log_cluster=True, centroids=8, grid=(2, 4), align=64)
+W_B2 = tiny(text_len=0, frames=3, lh=8, lw=12, bq=32, bk=32, D=64, H=3, B=2, dtype="bf16", mode="topk",
+            topk=0, keep_ratio=0.2, centroids=8, grid=(2, 4), align=32)
+
+
+def _scores(w, q, k, v):
+    g = _geo(w)
+    qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
+    kp = bsa.bsa_pool_blocks(kd, g, g.k_block)
+    vp = bsa.bsa_pool_blocks(vd, g, g.k_block)
+    P = bsa.bsa_cluster_importance(qd, kp, g, 1, 1, w.log_cluster)
+    return g, qd, kd, vd, P, vp
+
+
+def _check(w, P, vp, domain, value_aware, p, frame0, text):
+    g = geometry_of(w)
+    gg = _geo(w)
+    mask, cnt, idx, ent = bsa.bsa_select_top_p(P, gg, domain=domain, top_p=p, v_pooled=vp,
+                                               value_aware=value_aware, entropy_eps=1e-12,
+                                               frame0_dense=frame0, text_columns=text)
+    torch.cuda.synchronize()
+    Ph = P.cpu().numpy()
+    vph = vp.cpu().numpy() if value_aware else None
+    om, ocnt, oidx, oent = dm.select_top_p(Ph, g, domain, p, vp=vph, eps=1e-12, frame0_dense=frame0,
+                                           text_columns=text)
+    np.testing.assert_allclose(ent.cpu().numpy(), oent, rtol=1e-9)
+    srt = np.sort(oent, axis=1)
+    H = g.H
+    if H >= 2:                                    # the split is unambiguous on these inputs
+        assert (srt[:, H // 2] - srt[:, H // 2 - 1] > 1e-6 * np.abs(srt).max()).all()
+    assert np.array_equal(mask.cpu().numpy().astype(bool), om), domain
+    c = cnt.cpu().numpy()
+    assert np.array_equal(c, ocnt), domain
+    ih = idx.cpu().numpy()
+    for b in range(g.B):
+        for h in range(g.H):
+            for i in range(g.nqb):
+                n = ocnt[b, h, i]
+                assert np.array_equal(ih[b, h, i, :n], oidx[b, h, i, :n]), (domain, b, h, i)
+    return cnt, idx
+
+
+@pytest.mark.parametrize("domain", ["row", "head", "split", "all", "eg"])
+@pytest.mark.parametrize("value_aware", [False, True])
+def test_domains_small(domain, value_aware):
+    w = W_SMALL
+    _say(f"[gpu] top-p domain={domain} value_aware={value_aware}")
+    q, k, v = inputs_of(w)
+    g, qd, kd, vd, P, vp = _scores(w, q, k, v)
+    # the scores are the oracle's P' bit for bit
+    og = geometry_of(w)
+    oP = oracle.cluster_importance(q, oracle.pool_blocks(k, og.S, og.k_block), og, 1, 1, w.log_cluster)
+    assert np.array_equal(P.cpu().numpy(), oP)
+    _check(w, P, vp, domain, value_aware, 0.9, frame0=True, text=True)
+
+
+@pytest.mark.parametrize("domain", ["split", "eg", "all"])
+def test_domains_two_batch_elements_and_forward(domain):
+    w = W_B2
+    _say(f"[gpu] top-p B=2 domain={domain}")
+    q, k, v = inputs_of(w, pad_value=np.nan)
+    g, qd, kd, vd, P, vp = _scores(w, q, k, v)
+    cnt, idx = _check(w, P, vp, domain, True, 0.7, frame0=False, text=False)
+    out, _ = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None)
+    torch.cuda.synchronize()
+    og = geometry_of(w)
+    o = out.float().cpu().numpy()
+    ch, ih = cnt.cpu().numpy(), idx.cpu().numpy()
+    for b in range(og.B):
+        for h in range(og.H):
+            ref, _ = oracle.attention_head(q[b, h], k[b, h], v[b, h], og, ch[b, h], ih[b, h],
+                                           np.zeros((og.nqb, og.nkb), np.float32))
+            assert np.abs(o[b, h, :ref.shape[0]] - ref).max() <= 2e-2
+
+
+def test_eg_routing_full_size():
+    """The headline geometry: EG-Sparse routing with value-aware pooled scores, every row."""
+    w = W.workload("wan_1p3b_keep10")
+    _say("[gpu] top-p full-size eg value-aware")
+    q, k, v = inputs_of(w)
+    g, qd, kd, vd, P, vp = _scores(w, q, k, v)
+    _check(w, P, vp, "eg", True, 0.9, frame0=True, text=False)
