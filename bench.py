@@ -40,6 +40,7 @@ def _args():
     ap.add_argument("--cluster-clusters", type=int, default=4,
                     help="also time the intra-block clustering selector with this many clusters (0: skip)")
     ap.add_argument("--cluster-iters", type=int, default=3)
+    ap.add_argument("--no-top-p", action="store_true", help="skip the top-p domain selector timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -146,6 +147,46 @@ def cluster_selector_timing(bsa, w, g, p, qd, kp, C, T, nqb, nkb, stream, ev, re
             "roofline": {"bound": "alu", "kernel": "importance_kernel", "achieved": round(tops, 2),
                          "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s",
                          "frac": round(tops / PEAK_VALU_TLANEOPS, 4)}}
+
+
+def top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, reps=20):
+    """EG-Sparse routing (low-entropy heads pooled with value-aware scores, the
+    rest per-row local), top-p 0.9, on P' of the same inputs (one cluster).
+
+    Not part of the timed step.  Algorithmic bytes: the scores are read by the
+    entropy, total, four radix and selection passes (7 reads of B*H*nqb*nkb
+    floats) and the mask, counts and lists written once.
+    """
+    import ctypes
+    import numpy as np
+    import torch
+    vp = bsa.bsa_pool_blocks(vd, g, g.k_block)
+    P = bsa.bsa_cluster_importance(qd, kp, g, 1, 1, w.log_cluster)
+    nbytes = ctypes.c_int64()
+    bsa._lib.check(bsa._lib.lib().bsa_top_p_workspace_bytes(ctypes.byref(g.c()), ctypes.byref(nbytes)))
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=qd.device)
+    for _ in range(3):
+        bsa.bsa_select_top_p(P, g, "eg", 0.9, v_pooled=vp, value_aware=True, frame0_dense=w.frame0_dense,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e = [ev() for _ in range(2)]
+        e[0].record(stream)
+        mask, cnt, idx, ent = bsa.bsa_select_top_p(P, g, "eg", 0.9, v_pooled=vp, value_aware=True,
+                                                   frame0_dense=w.frame0_dense, workspace=ws)
+        e[1].record(stream)
+        ts.append(e)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ts]))
+    n = w.B * w.H * nqb * nkb
+    kept = int(cnt.sum().item())
+    byts = 7.0 * n * 4 + n + 4.0 * kept + w.B * w.H * nqb * 4
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"domain": "eg", "value_aware": True, "top_p": 0.9, "select_ms": round(ms, 4),
+            "executed_blocks": kept,
+            "roofline": {"bound": "hbm", "kernel": "tp_* (selection passes)", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
 def main():
@@ -267,6 +308,8 @@ def main():
     if a.cluster_clusters > 0 and a.cluster_clusters * nkb <= 16384:
         res["cluster_selector"] = cluster_selector_timing(bsa, w, g, p, qd, kp, a.cluster_clusters,
                                                           a.cluster_iters, nqb, nkb, stream, ev)
+    if not a.no_top_p and nkb <= 2048:
+        res["top_p_selector"] = top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks, a.cpu_sample_heads)
     res["input_gen_s"] = round(t_gen, 1)
