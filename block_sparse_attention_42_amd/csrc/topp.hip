@@ -17,15 +17,19 @@
 // kept.
 //
 // Kernels, in launch order (grid-wide dependencies between them):
-//   tp_row_entropy  one workgroup per row: sum_j -P log(P + eps) (float64)
-//   tp_heads        one workgroup per batch element: head entropies, median
-//                   split, pool of every head, pool state cleared
-//   tp_value_norm   norm of every pooled value row (value-aware scores)
-//   tp_total        one workgroup per pooled row: its mass into the pool total
-//   tp_target       per pool: target = ceil(p * total)
-//   tp_hist, tp_digit (x4)  radix passes of the pooled thresholds
-//   tp_select       one wave per row: threshold (pool's, or its own search),
-//                   safeguard, frame-0 rows, text columns, compaction
+//   tp_row_entropy    one workgroup per row: sum_j -P log(P + eps) (float64)
+//   tp_head_entropy   one workgroup per head: the mean over its rows
+//   tp_pools          one workgroup per batch element: median split, pool of
+//                     every head, pool state cleared
+//   tp_value_norm     norm of every pooled value row (value-aware scores)
+//   tp_row_total      one wave per pooled row: its mass
+//   tp_pool_target    one workgroup per pool: total, target = ceil(p * total)
+//   tp_hist, tp_digit (x4)  radix passes of the pooled thresholds: integer
+//                     bin masses of 16 rows per workgroup, then per pool a
+//                     suffix scan picks the digit
+//   tp_select         one wave per row: threshold (the pool's, or its own
+//                     bitwise search), safeguard, frame-0 rows, text columns,
+//                     compaction
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -51,17 +55,22 @@ __device__ __forceinline__ unsigned long long fixed_mass(float s) {
 
 struct Ws {
   double* row_ent;        // [BH * nqb]
+  unsigned long long* row_tot;   // [BH * nqb]
   double* head_ent;       // [BH]
   int32_t* pool;          // [BH]
   float* vnorm;           // [BH * nkb]
   PoolState* ps;          // [npools]
 };
 
+constexpr int kRowsPerHist = 16;   // rows of one head per histogram workgroup
+
 __device__ __forceinline__ Ws ws_of(const TopPArgs& a) {
   char* p = reinterpret_cast<char*>(a.ws);
   Ws w;
   w.row_ent = reinterpret_cast<double*>(p);
   p += sizeof(double) * (size_t)a.BH * a.nqb;
+  w.row_tot = reinterpret_cast<unsigned long long*>(p);
+  p += sizeof(unsigned long long) * (size_t)a.BH * a.nqb;
   w.head_ent = reinterpret_cast<double*>(p);
   p += sizeof(double) * (size_t)a.BH;
   w.pool = reinterpret_cast<int32_t*>(p);
@@ -98,18 +107,31 @@ __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a) {
   if (threadIdx.x == 0) w.row_ent[row] = red[0];
 }
 
-__global__ __launch_bounds__(kTpThreads) void tp_heads(TopPArgs a) {
-  extern __shared__ double hent[];          // [H]
+__global__ __launch_bounds__(kTpThreads) void tp_head_entropy(TopPArgs a) {
+  __shared__ double red[kTpThreads];
+  const Ws w = ws_of(a);
+  const int bh = blockIdx.x;
+  const double* r = w.row_ent + (int64_t)bh * a.nqb;
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < a.nqb; i += kTpThreads) acc += r[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = kTpThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double e = red[0] / (double)a.nqb;
+    w.head_ent[bh] = e;
+    if (a.entropy_out) a.entropy_out[bh] = e;
+  }
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_pools(TopPArgs a) {
   const Ws w = ws_of(a);
   const int b = blockIdx.x;
   const int H = a.H;
-  for (int h = threadIdx.x; h < H; h += kTpThreads) {
-    double acc = 0.0;
-    const double* r = w.row_ent + ((int64_t)b * H + h) * a.nqb;
-    for (int i = 0; i < a.nqb; ++i) acc += r[i];
-    hent[h] = acc / (double)a.nqb;
-  }
-  __syncthreads();
+  const double* hent = w.head_ent + (int64_t)b * H;
   for (int h = threadIdx.x; h < H; h += kTpThreads) {
     int rank = 0;
     for (int o = 0; o < H; ++o) rank += (hent[o] < hent[h] || (hent[o] == hent[h] && o < h)) ? 1 : 0;
@@ -123,8 +145,6 @@ __global__ __launch_bounds__(kTpThreads) void tp_heads(TopPArgs a) {
       default: pid = -1; break;                                // per-row local
     }
     w.pool[b * H + h] = pid;
-    w.head_ent[b * H + h] = hent[h];
-    if (a.entropy_out) a.entropy_out[b * H + h] = hent[h];
   }
   // clear the state of this batch element's pools
   int lo, hi;
@@ -158,15 +178,37 @@ __global__ __launch_bounds__(kTpThreads) void tp_value_norm(TopPArgs a) {
   w.vnorm[(int64_t)bh * a.vstride + j] = __fsqrt_rn(acc);
 }
 
-__global__ __launch_bounds__(kTpThreads) void tp_total(TopPArgs a) {
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_row_total(TopPArgs a) {
+  const Ws w = ws_of(a);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
+  const int bh = (int)(row / a.nqb);
+  if (w.pool[bh] < 0) return;
+  unsigned long long acc = 0ull;
+  for (int j = lane; j < a.nkb; j += 64) acc += fixed_mass(score_of(a, w, bh, row, j, true));
+  acc = wave_sum_u64(acc);
+  if (lane == 0) w.row_tot[row] = acc;
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_pool_target(TopPArgs a) {
   __shared__ unsigned long long red[kTpThreads];
   const Ws w = ws_of(a);
-  const int64_t row = blockIdx.x;
-  const int bh = (int)(row / a.nqb);
-  const int pid = w.pool[bh];
-  if (pid < 0) return;                                       // uniform over the workgroup
+  const int q = blockIdx.x;
   unsigned long long acc = 0ull;
-  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) acc += fixed_mass(score_of(a, w, bh, row, j, true));
+  int mine = 0;
+  for (int bh = 0; bh < a.BH; ++bh) {
+    if (w.pool[bh] != q) continue;                           // uniform
+    const unsigned long long* rt = w.row_tot + (int64_t)bh * a.nqb;
+    for (int i = threadIdx.x; i < a.nqb; i += kTpThreads) acc += rt[i];
+    ++mine;
+  }
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int h = kTpThreads / 2; h > 0; h >>= 1) {
@@ -174,17 +216,10 @@ __global__ __launch_bounds__(kTpThreads) void tp_total(TopPArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    atomicAdd(&w.ps[pid].total, red[0]);
-    w.ps[pid].used = 1u;
-  }
-}
-
-__global__ __launch_bounds__(kTpThreads) void tp_target(TopPArgs a) {
-  const Ws w = ws_of(a);
-  for (int q = threadIdx.x; q < a.npools; q += kTpThreads) {
     PoolState* ps = w.ps + q;
-    if (!ps->used) continue;
-    ps->target = (unsigned long long)ceil(a.top_p * (double)ps->total);
+    ps->used = mine > 0 ? 1u : 0u;
+    ps->total = red[0];
+    ps->target = (unsigned long long)ceil(a.top_p * (double)red[0]);
     ps->rem = ps->target;
     ps->prefix = 0u;
   }
@@ -193,49 +228,54 @@ __global__ __launch_bounds__(kTpThreads) void tp_target(TopPArgs a) {
 __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
   __shared__ unsigned long long bins[256];
   const Ws w = ws_of(a);
-  const int64_t row = blockIdx.x;
-  const int bh = (int)(row / a.nqb);
+  const int groups = (a.nqb + kRowsPerHist - 1) / kRowsPerHist;
+  const int bh = blockIdx.x / groups;
+  const int i0 = (blockIdx.x % groups) * kRowsPerHist;
   const int pid = w.pool[bh];
   if (pid < 0) return;
   bins[threadIdx.x] = 0ull;
   __syncthreads();
   const uint32_t prefix = w.ps[pid].prefix;
-  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
-    const float s = score_of(a, w, bh, row, j, true);
-    const uint32_t k = okey(s);
-    const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u;
-    if (match) atomicAdd(&bins[(k >> shift) & 255u], fixed_mass(s));
+  const int i1 = min(i0 + kRowsPerHist, a.nqb);
+  for (int i = i0; i < i1; ++i) {
+    const int64_t row = (int64_t)bh * a.nqb + i;
+    for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
+      const float s = score_of(a, w, bh, row, j, true);
+      const uint32_t k = okey(s);
+      const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u;
+      if (match) atomicAdd(&bins[(k >> shift) & 255u], fixed_mass(s));
+    }
   }
   __syncthreads();
   const unsigned long long v = bins[threadIdx.x];
   if (v) atomicAdd(&w.ps[pid].bins[threadIdx.x], v);
 }
 
+// per pool: suffix sums of the bins (mass of digits >= d inside the current
+// prefix group); the digit is the largest d whose suffix reaches the
+// remaining target, and the mass of the larger digits leaves the target
 __global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
+  __shared__ unsigned long long suf[257];
   const Ws w = ws_of(a);
-  for (int q = threadIdx.x; q < a.npools; q += kTpThreads) {
-    PoolState* ps = w.ps + q;
-    if (!ps->used) continue;
-    unsigned long long acc = 0ull;
-    int digit = 0;
-    for (int d = 255; d >= 0; --d) {
-      const unsigned long long bd = ps->bins[d];
-      if (acc + bd >= ps->rem) {
-        digit = d;
-        ps->rem -= acc;                                     // mass of larger digits in the group
-        break;
-      }
-      acc += bd;
-    }
-    ps->prefix |= (uint32_t)digit << shift;
-    for (int d = 0; d < 256; ++d) ps->bins[d] = 0ull;
+  PoolState* ps = w.ps + blockIdx.x;
+  if (!ps->used) return;                                     // uniform
+  const int d = threadIdx.x;
+  suf[d] = ps->bins[d];
+  if (d == 0) suf[256] = 0ull;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {                        // suffix scan, integer: any order is exact
+    const unsigned long long v = d + o < 256 ? suf[d + o] : 0ull;
+    __syncthreads();
+    suf[d] += v;
+    __syncthreads();
   }
-}
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-  return v;
+  const unsigned long long rem = ps->rem;
+  __syncthreads();
+  if (suf[d] >= rem && suf[d + 1] < rem) {
+    ps->rem = rem - suf[d + 1];
+    ps->prefix |= (uint32_t)d << shift;
+  }
+  ps->bins[d] = 0ull;
 }
 
 __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
@@ -330,30 +370,33 @@ __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
 
 int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb) {
   const int64_t npools = BH > 2 * B ? BH : 2 * B;
-  return (int64_t)sizeof(double) * BH * nqb + (int64_t)sizeof(double) * BH +
+  return (int64_t)sizeof(double) * BH * nqb + (int64_t)sizeof(unsigned long long) * BH * nqb +
+         (int64_t)sizeof(double) * BH +
          (int64_t)sizeof(int32_t) * ((BH + 1) / 2 * 2) + (int64_t)sizeof(float) * BH * ((nkb + 3) / 4 * 4) +
          (int64_t)sizeof(PoolState) * npools;
 }
 
 hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)((int64_t)a.BH * a.nqb);
+  const unsigned wave_groups = (unsigned)(((int64_t)a.BH * a.nqb + 3) / 4);
   hipLaunchKernelGGL(tp_row_entropy, dim3(rows), dim3(kTpThreads), 0, stream, a);
-  hipLaunchKernelGGL(tp_heads, dim3((unsigned)a.B), dim3(kTpThreads), sizeof(double) * a.H, stream, a);
+  hipLaunchKernelGGL(tp_head_entropy, dim3((unsigned)a.BH), dim3(kTpThreads), 0, stream, a);
+  hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
   if (a.value_aware) {
     const int64_t n = (int64_t)a.BH * a.nkb;
     hipLaunchKernelGGL(tp_value_norm, dim3((unsigned)((n + kTpThreads - 1) / kTpThreads)), dim3(kTpThreads), 0,
                        stream, a);
   }
   if (a.domain != 0) {
-    hipLaunchKernelGGL(tp_total, dim3(rows), dim3(kTpThreads), 0, stream, a);
-    hipLaunchKernelGGL(tp_target, dim3(1), dim3(kTpThreads), 0, stream, a);
+    hipLaunchKernelGGL(tp_row_total, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+    hipLaunchKernelGGL(tp_pool_target, dim3((unsigned)a.npools), dim3(kTpThreads), 0, stream, a);
+    const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + kRowsPerHist - 1) / kRowsPerHist));
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hipLaunchKernelGGL(tp_hist, dim3(rows), dim3(kTpThreads), 0, stream, a, shift);
-      hipLaunchKernelGGL(tp_digit, dim3(1), dim3(kTpThreads), 0, stream, a, shift);
+      hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, shift);
+      hipLaunchKernelGGL(tp_digit, dim3((unsigned)a.npools), dim3(kTpThreads), 0, stream, a, shift);
     }
   }
-  const unsigned groups = (unsigned)(((int64_t)a.BH * a.nqb + 3) / 4);
-  hipLaunchKernelGGL(tp_select, dim3(groups), dim3(kTpThreads), 0, stream, a);
+  hipLaunchKernelGGL(tp_select, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
   return hipGetLastError();
 }
 
