@@ -3,7 +3,9 @@
 Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py``; the library never imports, links or runs it.  See
 ``oracle/reference.py`` for the definitions and the pages they follow, and
-``oracle/cluster_select.py`` for the intra-block clustering selector.
+``oracle/cluster_select.py`` for the intra-block clustering selector,
+``oracle/domains.py`` for top-p over competition domains and
+``oracle/structured.py`` for the structured (per-head frame context) lists.
 """
 from .reference import *  # noqa: F401,F403
 from .reference import (Geometry, MaskParams, attention, attention_head, block_logits,  # noqa: F401
