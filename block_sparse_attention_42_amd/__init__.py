@@ -27,7 +27,8 @@ from ._lib import BsaError
 
 __all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
            "bsa_build_mask", "bsa_forward", "bsa_cluster_importance", "bsa_select_blocks",
-           "bsa_select_top_p", "DOMAINS", "library_path"]
+           "bsa_select_top_p", "DOMAINS", "HEAD_CLASSES", "bsa_frame_scores", "bsa_classify_heads",
+           "bsa_structured_lists", "library_path"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -234,6 +235,47 @@ def bsa_select_top_p(scores: torch.Tensor, g: Geometry, domain: str = "eg", top_
                                            workspace.numel(), _ptr(mask), _ptr(cnt), _ptr(idx),
                                            _stream(stream)))
     return mask, cnt, idx, ent
+
+
+HEAD_CLASSES = {"full": 0, "sink": 1, "neighbor": 2, "dummy": 3}
+
+
+def bsa_frame_scores(scores: torch.Tensor, g: Geometry, window: int, stream=None) -> torch.Tensor:
+    """Frame attention scores [B,H,3] float64 (sink, neighbor, current) from P' [B,H,nqb,nkb]."""
+    d = bsa_derive(g)
+    _need(scores, "scores", (g.B, g.H, d["nqb"], d["nkb"]), torch.float32)
+    alpha = torch.empty((g.B, g.H, 3), dtype=torch.float64, device=scores.device)
+    _lib.check(_lib.lib().bsa_frame_scores(_ptr(scores), ctypes.byref(g.c()), int(window), _ptr(alpha),
+                                           _stream(stream)))
+    return alpha
+
+
+def bsa_classify_heads(alpha, n_dummy: int):
+    """Host-side head labelling (numpy or CPU tensor alpha [B,H,3]) -> numpy int32 [B,H]."""
+    import numpy as np
+    a = np.ascontiguousarray(alpha.cpu().numpy() if isinstance(alpha, torch.Tensor) else alpha, dtype=np.float64)
+    B, H, _ = a.shape
+    out = np.empty((B, H), dtype=np.int32)
+    _lib.check(_lib.lib().bsa_classify_heads(a.ctypes.data, B, H, int(n_dummy), out.ctypes.data))
+    return out
+
+
+def bsa_structured_lists(head_class: torch.Tensor, g: Geometry, window: int, dummy_prev: bool = False,
+                         block_causal: bool = False, frame0_dense: bool = False, text_columns: bool = False,
+                         want_mask: bool = True, stream=None):
+    """Per-head frame-context lists -> (mask u8 or None, kv_cnt i32, kv_idx i32)."""
+    d = bsa_derive(g)
+    nqb, nkb = d["nqb"], d["nkb"]
+    dev = head_class.device
+    _need(head_class, "head_class", (g.B, g.H), torch.int32)
+    mask = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.uint8, device=dev) if want_mask else None
+    cnt = torch.empty((g.B, g.H, nqb), dtype=torch.int32, device=dev)
+    idx = torch.empty((g.B, g.H, nqb, nkb), dtype=torch.int32, device=dev)
+    sp = _lib.bsa_struct_params(int(window), 1 if dummy_prev else 0, 1 if block_causal else 0,
+                                1 if frame0_dense else 0, 1 if text_columns else 0, 0)
+    _lib.check(_lib.lib().bsa_structured_lists(_ptr(head_class), ctypes.byref(g.c()), ctypes.byref(sp), _ptr(mask),
+                                               _ptr(cnt), _ptr(idx), _stream(stream)))
+    return mask, cnt, idx
 
 
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,

@@ -16,6 +16,7 @@ BSA_SELECT_SAMPLE = 1
 
 EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward",
             "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes", "bsa_select_top_p",
+            "bsa_frame_scores", "bsa_classify_heads", "bsa_structured_lists",
             "bsa_status_string", "bsa_last_error", "bsa_abi_version"]
 
 
@@ -40,6 +41,12 @@ class bsa_topp_params(ctypes.Structure):
                 ("top_p", ctypes.c_double), ("entropy_eps", ctypes.c_float),
                 ("frame0_dense", ctypes.c_int32), ("text_columns", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class bsa_struct_params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("dummy_prev", ctypes.c_int32),
+                ("block_causal", ctypes.c_int32), ("frame0_dense", ctypes.c_int32),
+                ("text_columns", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class bsa_derived(ctypes.Structure):
@@ -73,9 +80,12 @@ def lib():
         L.bsa_top_p_workspace_bytes.argtypes = [G, ctypes.POINTER(ctypes.c_int64)]
         L.bsa_select_top_p.argtypes = [P, P, G, ctypes.POINTER(bsa_topp_params), P, P, ctypes.c_int64,
                                        P, P, P, P]
+        L.bsa_frame_scores.argtypes = [P, G, ctypes.c_int32, P, P]
+        L.bsa_classify_heads.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
+        L.bsa_structured_lists.argtypes = [P, G, ctypes.POINTER(bsa_struct_params), P, P, P, P]
         for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_abi_version",
                   "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes",
-                  "bsa_select_top_p"):
+                  "bsa_select_top_p", "bsa_frame_scores", "bsa_classify_heads", "bsa_structured_lists"):
             getattr(L, f).restype = ctypes.c_int32
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p

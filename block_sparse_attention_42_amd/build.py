@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libbsa.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "topp.hip", "forward.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "topp.hip", "structured.hip", "forward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are switched off for every device pass.

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/bsa.h"
 #include "bsa_internal.h"
@@ -363,6 +364,94 @@ bsa_status bsa_select_top_p(const float* scores, const float* v_pooled, const bs
   a.text_last = tp->text_columns ? d.text_last : -1;
   hipError_t e = bsa::launch_topp(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "top-p launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_frame_scores(const float* scores, const bsa_geometry* g, int32_t window, double* alpha,
+                            void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (!scores || !alpha) return fail(BSA_ERR_INVALID_ARGUMENT, "scores and alpha must not be NULL");
+  if (!aligned16(scores) || !aligned16(alpha))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (window < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "window %d must be >= 1", window);
+  if ((int64_t)g->latent_h * g->latent_w < 1 || g->frames < 1)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "frame scores need frames and latent_h * latent_w >= 1");
+  bsa::StructArgs a = {};
+  a.scores = scores;
+  a.alpha = alpha;
+  a.S = d.S;
+  a.text_len = g->text_len;
+  a.tpf = (int64_t)g->latent_h * g->latent_w;
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.q_block = g->q_block;
+  a.k_block = g->k_block;
+  a.window = window;
+  hipError_t e = bsa::launch_frame_scores(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "frame-score launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsa_status bsa_classify_heads(const double* alpha, int32_t B, int32_t H, int32_t n_dummy, int32_t* classes) {
+  if (!alpha || !classes) return fail(BSA_ERR_INVALID_ARGUMENT, "alpha and classes must not be NULL");
+  if (B < 1 || H < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B=%d and H=%d must be >= 1", B, H);
+  if (n_dummy < 0 || n_dummy > H) return fail(BSA_ERR_INVALID_ARGUMENT, "n_dummy %d must be in 0..H", n_dummy);
+  for (int64_t t = 0; t < (int64_t)B * H * 3; ++t)
+    if (!std::isfinite(alpha[t])) return fail(BSA_ERR_INVALID_ARGUMENT, "alpha[%lld] is not finite", (long long)t);
+  std::vector<int32_t> order(H);
+  for (int32_t b = 0; b < B; ++b) {
+    const double* al = alpha + (int64_t)b * H * 3;
+    auto lh = [&](int32_t h) { return std::max(al[h * 3 + 0], al[h * 3 + 1]); };
+    for (int32_t h = 0; h < H; ++h) order[h] = h;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return lh(x) < lh(y); });
+    for (int32_t r = 0; r < H; ++r) {
+      const int32_t h = order[r];
+      classes[(int64_t)b * H + h] =
+          r < n_dummy ? BSA_HEAD_DUMMY : (al[h * 3 + 0] > al[h * 3 + 1] ? BSA_HEAD_SINK : BSA_HEAD_NEIGHBOR);
+    }
+  }
+  return ok();
+}
+
+bsa_status bsa_structured_lists(const int32_t* head_class, const bsa_geometry* g, const bsa_struct_params* sp,
+                                uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (!sp) return fail(BSA_ERR_INVALID_ARGUMENT, "structure params are NULL");
+  if (!head_class || !kv_cnt || !kv_idx)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "head_class, kv_cnt and kv_idx must not be NULL");
+  if (!aligned16(head_class) || !aligned16(kv_cnt) || !aligned16(kv_idx) || (mask && !aligned16(mask)))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "device buffers must be 16-byte aligned");
+  if (sp->window < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "window %d must be >= 1", sp->window);
+  if ((int64_t)g->latent_h * g->latent_w < 1 && g->frames > 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "latent_h * latent_w must be >= 1");
+  if ((int64_t)g->B * g->H * d.nqb > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+  bsa::StructArgs a = {};
+  a.classes = head_class;
+  a.mask = mask;
+  a.cnt = kv_cnt;
+  a.idx = kv_idx;
+  a.S = d.S;
+  a.text_len = g->text_len;
+  a.tpf = std::max<int64_t>(1, (int64_t)g->latent_h * g->latent_w);
+  a.BH = g->B * g->H;
+  a.nqb = d.nqb;
+  a.nkb = d.nkb;
+  a.q_block = g->q_block;
+  a.k_block = g->k_block;
+  a.window = sp->window;
+  a.dummy_prev = sp->dummy_prev ? 1 : 0;
+  a.block_causal = sp->block_causal ? 1 : 0;
+  a.frame0_first = sp->frame0_dense ? d.f0_first : -1;
+  a.frame0_last = sp->frame0_dense ? d.f0_last : -1;
+  a.text_last = sp->text_columns ? d.text_last : -1;
+  hipError_t e = bsa::launch_struct_lists(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "structured-list launch: %s", hipGetErrorString(e));
   return ok();
 }
 

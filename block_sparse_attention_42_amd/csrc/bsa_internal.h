@@ -64,6 +64,24 @@ struct TopPArgs {
   int32_t text_last;                   // -1 if off
 };
 
+// Launch arguments of the structured-list kernels (per-head frame contexts).
+struct StructArgs {
+  const float* scores;   // [BH, nqb, nkb] P' (frame scores) or null
+  double* alpha;         // [BH, 3] frame scores out
+  const int32_t* classes;   // [BH] head classes: 0 full, 1 sink, 2 neighbor, 3 dummy
+  uint8_t* mask;         // [BH, nqb, nkb] or null
+  int32_t* cnt;          // [BH, nqb]
+  int32_t* idx;          // [BH, nqb, nkb]
+  int64_t S;
+  int64_t text_len;
+  int64_t tpf;           // tokens per frame (>= 1)
+  int32_t BH, nqb, nkb, q_block, k_block;
+  int32_t window;        // L: frames a neighbor head sees, the current one included
+  int32_t dummy_prev, block_causal;
+  int32_t frame0_first, frame0_last;   // -1 if off
+  int32_t text_last;                   // -1 if off
+};
+
 // Launch arguments of the block-importance kernel (intra-block clusters).
 struct ImpArgs {
   const void* q;      // [BH, seq_alloc, D]
@@ -113,6 +131,8 @@ hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 size_t importance_lds_bytes(const ImpArgs& a);
 int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb);
 hipError_t launch_topp(const TopPArgs& a, hipStream_t stream);
+hipError_t launch_frame_scores(const StructArgs& a, hipStream_t stream);
+hipError_t launch_struct_lists(const StructArgs& a, hipStream_t stream);
 hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
 

@@ -14,8 +14,10 @@
  *      an optional additive per-block log-weight  (bsa_forward);
  *   and, as a finer selector, block importance from k-means representatives
  *   of each query block (bsa_cluster_importance) with selection from any
- *   importance matrix (bsa_select_blocks); and top-p selection over
- *   competition domains routed by per-head entropy (bsa_select_top_p).
+ *   importance matrix (bsa_select_blocks); top-p selection over competition
+ *   domains routed by per-head entropy (bsa_select_top_p); and structured
+ *   lists of per-head frame contexts (bsa_frame_scores, bsa_classify_heads,
+ *   bsa_structured_lists).
  *
  * Pages followed (title; section):
  *   - "Attention matrix view: make only frame-0 query rows dense": sec. 1
@@ -275,6 +277,69 @@ bsa_status bsa_select_top_p(const float* scores, const float* v_pooled, const bs
                             const bsa_topp_params* tp, double* head_entropy, void* workspace,
                             int64_t workspace_bytes, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx,
                             void* stream);
+
+/* Structured block lists: per-head frame contexts over the same forward
+ * ("Efficient Autoregressive Video Diffusion with Dummy Head": frame
+ * attention scores of its Step 0, Dynamic Head Programming of its Step 1 and
+ * worked example, the per-class contexts of its Steps 2-3; the block-causal
+ * frame mask of "Purpose of the block-causal mask ..."; frame-0 page sec. 1
+ * token packing).  Token t is text (frame -1) if t < text_len, else in frame
+ * (t - text_len) / (latent_h * latent_w); frame 0 is the sink frame. */
+typedef enum {
+  BSA_HEAD_FULL = 0,      /* every frame (frames <= the query's with block_causal) */
+  BSA_HEAD_SINK = 1,      /* the sink frame and the query's frame */
+  BSA_HEAD_NEIGHBOR = 2,  /* the last `window` frames, the query's included */
+  BSA_HEAD_DUMMY = 3      /* the query's frame (and the one before with dummy_prev) */
+} bsa_head_class;
+
+typedef struct {
+  int32_t window;         /* L >= 1 */
+  int32_t dummy_prev;     /* dummy heads also see frame i-1 (packed dummy heads) */
+  int32_t block_causal;   /* full heads see frames <= the query's only */
+  int32_t frame0_dense;   /* query blocks overlapping frame 0 keep every block */
+  int32_t text_columns;   /* every row keeps the key blocks overlapping the text */
+  int32_t reserved;
+} bsa_struct_params;
+
+/* Frame attention scores of every head from block scores.
+ *   scores: [B, H, nqb, nkb] float32 P' (e.g. bsa_cluster_importance, one
+ *           cluster).
+ *   window: L >= 1.
+ *   alpha:  [B, H, 3] float64 device buffer, written: for every query block
+ *           whose first token is in a frame f >= 1, the P' mass on key blocks
+ *           whose first token is in frame 0 (sink), in frames max(1, f-L+1)
+ *           .. f-1 (neighbor) and in frame f (current), normalized to sum 1;
+ *           the mean over those query blocks (0 if there are none).
+ *   Errors: NULL or misaligned buffers, window < 1, or no frames give
+ *   BSA_ERR_INVALID_ARGUMENT before any launch. */
+bsa_status bsa_frame_scores(const float* scores, const bsa_geometry* g, int32_t window, double* alpha,
+                            void* stream);
+
+/* Dynamic Head Programming on the host (no device work).
+ *   alpha:   host [B, H, 3] frame scores.  n_dummy: dummy heads per batch
+ *            element, 0..H.
+ *   classes: host [B, H] int32, written: the n_dummy heads of smallest
+ *            max(a_sink, a_neighbor) (lower head first among equals) are
+ *            BSA_HEAD_DUMMY, the others BSA_HEAD_SINK if a_sink > a_neighbor,
+ *            else BSA_HEAD_NEIGHBOR.
+ *   Errors: NULL pointers, B or H < 1, n_dummy outside 0..H, or a
+ *   non-finite alpha give BSA_ERR_INVALID_ARGUMENT; classes is then not
+ *   written. */
+bsa_status bsa_classify_heads(const double* alpha, int32_t B, int32_t H, int32_t n_dummy, int32_t* classes);
+
+/* Block lists of the per-head contexts.
+ *   head_class: [B, H] int32 device buffer of bsa_head_class values.
+ *   A query block's context is the union over the frames of its tokens of
+ *   its head class's frames, plus the text; a query block holding text sees
+ *   everything.  A key block is listed iff it holds a token of the context.
+ *   Frame-0 rows and text columns are applied after.  A class value other
+ *   than 0, 1 or 2 is read as BSA_HEAD_DUMMY.
+ *   mask (optional, NULL to skip), kv_cnt, kv_idx: as for bsa_build_mask
+ *   (lists ascending; entries past kv_cnt are not written).
+ *   Errors: NULL params, head_class, kv_cnt or kv_idx, a buffer not 16-byte
+ *   aligned or window < 1 give BSA_ERR_INVALID_ARGUMENT before any launch. */
+bsa_status bsa_structured_lists(const int32_t* head_class, const bsa_geometry* g, const bsa_struct_params* sp,
+                                uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, void* stream);
 
 const char* bsa_status_string(int32_t status);
 const char* bsa_last_error(void);

@@ -145,6 +145,23 @@ def test_validation_rejects_before_launch():
     bigger = _geo(W.workload("hunyuan_keep08").replace(k_block=32)).c()   # nkb 3721 > 2048
     L.bsa_top_p_workspace_bytes(ctypes.byref(bigger), ctypes.byref(nb))
     assert sel(tp(), geo=bigger) == _lib.BSA_ERR_UNSUPPORTED
+    # structured producers
+    assert L.bsa_frame_scores(fake, ctypes.byref(g), 0, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_frame_scores(None, ctypes.byref(g), 2, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_frame_scores(fake, ctypes.byref(g), 2, mis, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+
+    def sp(**kw):
+        base = dict(window=3, dummy_prev=0, block_causal=1, frame0_dense=0, text_columns=0, reserved=0)
+        base.update(kw)
+        return _lib.bsa_struct_params(**base)
+    assert L.bsa_structured_lists(fake, ctypes.byref(g), ctypes.byref(sp(window=0)), None, fake, fake, None) \
+        == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_structured_lists(fake, ctypes.byref(g), None, None, fake, fake, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_structured_lists(None, ctypes.byref(g), ctypes.byref(sp()), None, fake, fake, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_structured_lists(fake, ctypes.byref(g), ctypes.byref(sp()), mis, fake, fake, None) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
 
 
 def test_python_binding_raises_on_missing_gpu_tensors():
@@ -153,3 +170,33 @@ def test_python_binding_raises_on_missing_gpu_tensors():
     x = torch.zeros((1, 2, 224, 64))
     with pytest.raises(ValueError):
         bsa.bsa_pool_blocks(x, _geo(w), 32)     # CPU tensor: refused, never computed on the CPU
+
+
+def test_head_labelling_on_the_host_matches_the_oracle():
+    """bsa_classify_heads is host-only: the page's worked example and random scores
+    against the oracle's DHP."""
+    import json
+    import numpy as np
+    import oracle.structured as st
+    gd = json.load(open(os.path.join(ROOT, "tests", "golden", "dhp_example.json")))
+    lh = gd["max_sink_neighbor"]
+    alpha = np.zeros((1, len(lh), 3))
+    for h, l in enumerate(lh):
+        alpha[0, h] = [l, l / 2, 1 - l] if h % 2 else [l / 3, l, 1 - l]
+    cls = bsa.bsa_classify_heads(alpha, gd["n_dummy"])
+    assert sorted(np.nonzero(cls[0] == 3)[0].tolist()) == gd["dummy_heads"]
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 20))
+        a = rng.dirichlet([1, 1, 1], size=(B, H))
+        a[..., :2] = np.round(a[..., :2] * 8) / 8                  # ties
+        n = int(rng.integers(0, H + 1))
+        assert np.array_equal(bsa.bsa_classify_heads(a, n), st.classify_heads(a, n))
+    L = _lib.lib()
+    bad = np.zeros((1, 2, 3))
+    assert L.bsa_classify_heads(bad.ctypes.data, 1, 2, 3, np.zeros(2, np.int32).ctypes.data) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    bad[0, 1, 0] = np.nan
+    assert L.bsa_classify_heads(bad.ctypes.data, 1, 2, 1, np.zeros(2, np.int32).ctypes.data) == \
+        _lib.BSA_ERR_INVALID_ARGUMENT
+    assert b"finite" in L.bsa_last_error()
