@@ -41,6 +41,7 @@ def _args():
                     help="also time the intra-block clustering selector with this many clusters (0: skip)")
     ap.add_argument("--cluster-iters", type=int, default=3)
     ap.add_argument("--no-top-p", action="store_true", help="skip the top-p domain selector timing")
+    ap.add_argument("--no-structured", action="store_true", help="skip the structured-list producer timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -189,6 +190,73 @@ def top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, reps=20):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def structured_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, window=3, reps=20):
+    """Per-head frame contexts: frame scores of P' (one cluster), host-side head
+    labelling with half the heads dummy heads, block-causal full heads, neighbor
+    window 3; then the list producer and the forward on its lists (frame-run
+    launch order, and the default order for comparison).
+
+    Not part of the timed step.  Algorithmic bytes: the frame-score kernel reads
+    the P' entries of the sink, neighbor and current runs of every scored row;
+    the list producer writes the mask, counts and lists once.
+    """
+    import numpy as np
+    import torch
+    P = bsa.bsa_cluster_importance(qd, kp, g, 1, 1, w.log_cluster)
+    alpha = bsa.bsa_frame_scores(P, g, window)
+    cls = torch.from_numpy(bsa.bsa_classify_heads(alpha.cpu(), w.H // 2)).to(qd.device)
+    out = torch.empty_like(qd)
+
+    def lists():
+        return bsa.bsa_structured_lists(cls, g, window, block_causal=True, frame0_dense=w.frame0_dense)
+    for _ in range(3):
+        bsa.bsa_frame_scores(P, g, window)
+        _, cnt, idx = lists()
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, out=out, launch_order="frame_runs")
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, out=out)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e = [ev() for _ in range(5)]
+        e[0].record(stream)
+        bsa.bsa_frame_scores(P, g, window)
+        e[1].record(stream)
+        mask, cnt, idx = lists()
+        e[2].record(stream)
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, out=out, launch_order="frame_runs")
+        e[3].record(stream)
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, out=out)
+        e[4].record(stream)
+        ts.append(e)
+    torch.cuda.synchronize()
+    fs_ms, ls_ms, fw_ms, fp_ms = (float(np.mean([e[k].elapsed_time(e[k + 1]) for e in ts])) for k in range(4))
+    kept = int(cnt.sum().item())
+    # P' entries the frame-score kernel reads (integer geometry of the frame runs)
+    tpf = w.latent_h * w.latent_w
+
+    def first_block(f):
+        return -(-min(w.text_len + f * tpf, w.S) // w.k_block)
+    read = 0
+    for i in range(nqb):
+        t = i * w.q_block
+        f = -1 if t < w.text_len else (t - w.text_len) // tpf
+        if f >= 1:
+            read += first_block(1) - first_block(0) + first_block(f + 1) - first_block(max(1, f - window + 1))
+    fs_bytes = 4.0 * read * w.B * w.H
+    ls_bytes = w.B * w.H * nqb * (nkb + 4) + 4.0 * kept
+    gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
+    tf = 4.0 * w.D * w.q_block * w.k_block * kept / (fw_ms * 1e-3) / 1e12
+    counts = {c: int((cls.cpu() == i).sum()) for i, c in enumerate(("full", "sink", "neighbor", "dummy"))}
+    return {"window": window, "heads": counts, "block_causal": True,
+            "frame_scores_ms": round(fs_ms, 4), "frame_scores_gbs": round(fs_bytes / (fs_ms * 1e-3) / 1e9, 1),
+            "lists_ms": round(ls_ms, 4), "executed_blocks": kept,
+            "density": round(kept / (w.B * w.H * nqb * nkb), 4),
+            "fwd_launch_order": "frame_runs", "fwd_ms": round(fw_ms, 4), "fwd_tflops": round(tf, 2),
+            "fwd_ms_frame_position_order": round(fp_ms, 4),
+            "roofline": {"bound": "hbm", "kernel": "struct_lists_kernel", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     a = _args()
     if a.calibrate_copy_mib:
@@ -310,6 +378,8 @@ def main():
                                                           a.cluster_iters, nqb, nkb, stream, ev)
     if not a.no_top_p and nkb <= 2048:
         res["top_p_selector"] = top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev)
+    if not a.no_structured:
+        res["structured_lists"] = structured_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks, a.cpu_sample_heads)
     res["input_gen_s"] = round(t_gen, 1)

@@ -27,7 +27,7 @@ from ._lib import BsaError
 
 __all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
            "bsa_build_mask", "bsa_forward", "bsa_cluster_importance", "bsa_select_blocks",
-           "bsa_select_top_p", "DOMAINS", "HEAD_CLASSES", "bsa_frame_scores", "bsa_classify_heads",
+           "bsa_select_top_p", "DOMAINS", "HEAD_CLASSES", "LAUNCH_ORDERS", "bsa_frame_scores", "bsa_classify_heads",
            "bsa_structured_lists", "library_path"]
 
 
@@ -238,6 +238,7 @@ def bsa_select_top_p(scores: torch.Tensor, g: Geometry, domain: str = "eg", top_
 
 
 HEAD_CLASSES = {"full": 0, "sink": 1, "neighbor": 2, "dummy": 3}
+LAUNCH_ORDERS = {"frame_position": 0, "frame_runs": 1}
 
 
 def bsa_frame_scores(scores: torch.Tensor, g: Geometry, window: int, stream=None) -> torch.Tensor:
@@ -281,8 +282,14 @@ def bsa_structured_lists(head_class: torch.Tensor, g: Geometry, window: int, dum
 def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
                 kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
-    """Attention of every query block over its listed key blocks.  Returns (out, lse or None)."""
+                lse: Optional[torch.Tensor] = None, want_lse: bool = False, launch_order: str = "frame_position",
+                stream=None):
+    """Attention of every query block over its listed key blocks.  Returns (out, lse or None).
+
+    ``launch_order`` ("frame_position" or "frame_runs", see LAUNCH_ORDERS) only
+    changes which work items run together; "frame_runs" calls bsa_forward_ex."""
+    if launch_order not in LAUNCH_ORDERS:
+        raise ValueError(f"launch_order {launch_order!r} not in {sorted(LAUNCH_ORDERS)}")
     d = bsa_derive(g)
     nqb, nkb = d["nqb"], d["nkb"]
     shape = (g.B, g.H, g.seq_alloc, g.head_dim)
@@ -301,8 +308,11 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
         lse = torch.empty((g.B, g.H, g.seq_alloc), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", (g.B, g.H, g.seq_alloc), torch.float32, dev)
-    _lib.check(_lib.lib().bsa_forward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()),
-                                      _ptr(kv_cnt), _ptr(kv_idx), _ptr(log_w),
-                                      ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse),
-                                      _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()), _ptr(kv_cnt), _ptr(kv_idx),
+            _ptr(log_w), ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse))
+    if launch_order == "frame_position":
+        _lib.check(_lib.lib().bsa_forward(*args, _stream(stream)))
+    else:
+        opt = _lib.bsa_forward_options(LAUNCH_ORDERS[launch_order])
+        _lib.check(_lib.lib().bsa_forward_ex(*args, ctypes.byref(opt), _stream(stream)))
     return out, lse

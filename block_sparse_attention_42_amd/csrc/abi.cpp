@@ -378,12 +378,15 @@ bsa_status bsa_frame_scores(const float* scores, const bsa_geometry* g, int32_t 
   if (window < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "window %d must be >= 1", window);
   if ((int64_t)g->latent_h * g->latent_w < 1 || g->frames < 1)
     return fail(BSA_ERR_INVALID_ARGUMENT, "frame scores need frames and latent_h * latent_w >= 1");
+  if (g->frames > bsa::kMaxStructFrames)
+    return fail(BSA_ERR_UNSUPPORTED, "frames %d > %d", g->frames, bsa::kMaxStructFrames);
   bsa::StructArgs a = {};
   a.scores = scores;
   a.alpha = alpha;
   a.S = d.S;
   a.text_len = g->text_len;
   a.tpf = (int64_t)g->latent_h * g->latent_w;
+  a.frames = g->frames;
   a.BH = g->B * g->H;
   a.nqb = d.nqb;
   a.nkb = d.nkb;
@@ -439,6 +442,7 @@ bsa_status bsa_structured_lists(const int32_t* head_class, const bsa_geometry* g
   a.S = d.S;
   a.text_len = g->text_len;
   a.tpf = std::max<int64_t>(1, (int64_t)g->latent_h * g->latent_w);
+  a.frames = g->frames;
   a.BH = g->B * g->H;
   a.nqb = d.nqb;
   a.nkb = d.nkb;
@@ -459,6 +463,16 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
                        const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
                        const float* log_w, float softmax_scale, void* out, float* lse,
                        void* stream) {
+  return bsa_forward_ex(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, nullptr, stream);
+}
+
+bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t dtype,
+                          const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                          const float* log_w, float softmax_scale, void* out, float* lse,
+                          const bsa_forward_options* opt, void* stream) {
+  const int32_t order = opt ? opt->launch_order : BSA_ORDER_FRAME_POSITION;
+  if (order != BSA_ORDER_FRAME_POSITION && order != BSA_ORDER_FRAME_RUNS)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown launch order %d", order);
   Derived d;
   bsa_status s = check_geometry(g, &d);
   if (s != BSA_OK) return s;
@@ -501,7 +515,10 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
   const int32_t nd = d.f0_first >= 0 ? d.f0_last - d.f0_first + 1 : 0;
   a.n_dense = a.BH * nd;
   const int64_t n_other = (int64_t)a.BH * (d.nqb - nd);
-  a.per_xcd = (int32_t)((n_other + bsa::kXcds - 1) / bsa::kXcds);
+  a.order = order;
+  a.per_xcd = order == BSA_ORDER_FRAME_RUNS
+                  ? (int32_t)((int64_t)a.BH * ((d.nqb - nd + bsa::kXcds - 1) / bsa::kXcds))
+                  : (int32_t)((n_other + bsa::kXcds - 1) / bsa::kXcds);
   if (bsa::forward_grid(a) > 0x7fffffffLL) return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
   hipError_t e = bsa::launch_forward(a, dtype, g->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

@@ -65,6 +65,8 @@ struct TopPArgs {
 };
 
 // Launch arguments of the structured-list kernels (per-head frame contexts).
+constexpr int kMaxStructFrames = 4096;   // frame-score table in LDS
+
 struct StructArgs {
   const float* scores;   // [BH, nqb, nkb] P' (frame scores) or null
   double* alpha;         // [BH, 3] frame scores out
@@ -75,6 +77,7 @@ struct StructArgs {
   int64_t S;
   int64_t text_len;
   int64_t tpf;           // tokens per frame (>= 1)
+  int32_t frames;        // latent frames (<= kMaxStructFrames for frame scores)
   int32_t BH, nqb, nkb, q_block, k_block;
   int32_t window;        // L: frames a neighbor head sees, the current one included
   int32_t dummy_prev, block_causal;
@@ -116,13 +119,16 @@ struct FwdArgs {
   int32_t period;                    // query blocks per frame, rounded (>= 1)
   int32_t per_xcd;                   // remaining work items per XCD
   int32_t n_dense;                   // BH * dense rows
+  int32_t order;                     // 0: frame-position runs, 1: frame runs of every head
 };
 
 // Work items of the forward launch: the frame-0 (longest) rows of every head
-// first, dealt round-robin over the XCDs, then the other rows in contiguous
-// per-XCD runs of consecutive work items (head-major; inside a head, query
-// blocks at the same in-frame position of successive frames are adjacent), so
-// that rows running together on one XCD share key blocks in its L2.
+// first, dealt round-robin over the XCDs, then the other rows.  Order 0: in
+// contiguous per-XCD runs of consecutive work items (head-major; inside a
+// head, query blocks at the same in-frame position of successive frames are
+// adjacent), so that rows running together on one XCD share key blocks in
+// its L2.  Order 1: XCD x takes the x-th eighth of every head's other rows
+// (a run of frames), head-major, in index order.
 constexpr int kXcds = 8;
 inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int64_t)kXcds * a.per_xcd; }
 

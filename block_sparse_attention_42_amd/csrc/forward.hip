@@ -184,6 +184,15 @@ __device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& 
   const int ns = a.nqb - nd;                       // other rows per head
   const int x = t % kXcds, k = t / kXcds;
   const int k0 = (a.n_dense + kXcds - 1 - x) / kXcds;
+  if (a.order == 1) {                              // the x-th run of frames of every head
+    const int lo = (int)((int64_t)x * ns / kXcds), len = (int)((int64_t)(x + 1) * ns / kXcds) - lo;
+    const int pos = k - k0;
+    if (pos >= a.BH * len) return false;           // also every item when len == 0
+    bh = pos / len;
+    const int s = lo + pos % len;
+    qb = (a.dense_first < 0 || s < a.dense_first) ? s : s + nd;
+    return true;
+  }
   const int ls = x * a.per_xcd + (k - k0);         // rank among the other rows
   if (ls >= a.BH * ns) return false;
   bh = ls / ns;

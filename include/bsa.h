@@ -184,6 +184,32 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
                        const float* log_w, float softmax_scale, void* out, float* lse,
                        void* stream);
 
+/* Launch order of the forward's work items.  Performance only: every row is
+ * computed the same way, so the outputs are bit-identical under either. */
+typedef enum {
+  /* default: each XCD takes a contiguous run of (head, query block) items;
+   * inside a head, query blocks at the same in-frame position of successive
+   * frames run together (content-selected lists overlap most there) */
+  BSA_ORDER_FRAME_POSITION = 0,
+  /* each XCD takes the same run of frames of every head: for frame-banded
+   * lists (bsa_structured_lists), whose length differs by head class, this
+   * balances the XCDs and keeps each XCD's keys inside its frames */
+  BSA_ORDER_FRAME_RUNS = 1
+} bsa_launch_order;
+
+typedef struct {
+  int32_t launch_order;   /* bsa_launch_order */
+  int32_t reserved[3];
+} bsa_forward_options;
+
+/* bsa_forward with options (NULL: the defaults).  An unknown launch order
+ * gives BSA_ERR_INVALID_ARGUMENT before any launch; everything else as
+ * bsa_forward. */
+bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t dtype,
+                          const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                          const float* log_w, float softmax_scale, void* out, float* lse,
+                          const bsa_forward_options* opt, void* stream);
+
 /* Intra-block clustering selector, step 1: block importance (AB-Attention
  * page, TL;DR item 1 and the flowchart's intra-block cluster node: queries
  * are clustered only inside their own query block; EG-Sparse page Eq. 2 for
@@ -311,7 +337,8 @@ typedef struct {
  *           .. f-1 (neighbor) and in frame f (current), normalized to sum 1;
  *           the mean over those query blocks (0 if there are none).
  *   Errors: NULL or misaligned buffers, window < 1, or no frames give
- *   BSA_ERR_INVALID_ARGUMENT before any launch. */
+ *   BSA_ERR_INVALID_ARGUMENT, more than 4096 frames BSA_ERR_UNSUPPORTED,
+ *   before any launch. */
 bsa_status bsa_frame_scores(const float* scores, const bsa_geometry* g, int32_t window, double* alpha,
                             void* stream);
 

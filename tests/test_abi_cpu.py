@@ -145,6 +145,11 @@ def test_validation_rejects_before_launch():
     bigger = _geo(W.workload("hunyuan_keep08").replace(k_block=32)).c()   # nkb 3721 > 2048
     L.bsa_top_p_workspace_bytes(ctypes.byref(bigger), ctypes.byref(nb))
     assert sel(tp(), geo=bigger) == _lib.BSA_ERR_UNSUPPORTED
+    # forward options
+    bad_order = _lib.bsa_forward_options(7)
+    assert L.bsa_forward_ex(fake, fake, fake, 0, ctypes.byref(g), fake, fake, None, 0.0, fake, None,
+                            ctypes.byref(bad_order), None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert b"launch order" in L.bsa_last_error()
     # structured producers
     assert L.bsa_frame_scores(fake, ctypes.byref(g), 0, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert L.bsa_frame_scores(None, ctypes.byref(g), 2, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT

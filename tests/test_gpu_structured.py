@@ -132,7 +132,7 @@ def test_frame_scores_labels_and_forward(name, window):
     assert np.array_equal(cls, st.classify_heads(ga, n_dummy))
     assert ((cls == st.DUMMY).sum(-1) == n_dummy).all()
     cnt, idx = _compare(w, cls, window, True, True, frame0=True, text=True)
-    out, _ = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None)
+    out, _ = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, launch_order="frame_runs")
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     ch, ih = cnt.cpu().numpy(), idx.cpu().numpy()
@@ -151,3 +151,29 @@ def test_lists_full_size():
     _say("[gpu] structured lists full size, one head per class")
     cls = np.array([[st.FULL, st.SINK, st.NEIGHBOR, st.DUMMY]], dtype=np.int32)
     _compare(w, cls, 3, True, True, frame0=True, text=False)
+
+
+@pytest.mark.parametrize("name", ["aligned", "straddle", "headline"])
+def test_launch_orders_give_identical_outputs(name):
+    """The launch order only moves work items between XCDs: outputs and LSE are
+    bit-identical, for structured lists and for top-k lists (the aligned
+    geometry has fewer other rows than XCDs, so some XCDs get none)."""
+    w = W.workload("wan_1p3b_keep10") if name == "headline" else GEOS[name]
+    _say(f"[gpu] launch orders {name}")
+    q, k, v = inputs_of(w)
+    g = _geo(w)
+    qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
+    cls = torch.from_numpy(_classes(w.B, w.H, 3)).cuda()
+    _, c1, i1 = bsa.bsa_structured_lists(cls, g, 3, block_causal=True, frame0_dense=True, want_mask=False)
+    p = bsa.MaskParams(mode="topk", topk=0, keep_ratio=0.1, frame0_dense=True, text_columns=False,
+                       log_cluster=False, seed=0)
+    qp = bsa.bsa_pool_blocks(qd, g, g.q_block)
+    kp = bsa.bsa_pool_blocks(kd, g, g.k_block)
+    _, c2, i2, _ = bsa.bsa_build_mask(qp, kp, g, p)
+    for cnt, idx in ((c1, i1), (c2, i2)):
+        o1, l1 = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, want_lse=True)
+        o2, l2 = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, want_lse=True, launch_order="frame_runs")
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1,
+                           o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2)
+        assert torch.equal(l1, l2)
