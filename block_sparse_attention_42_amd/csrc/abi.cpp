@@ -252,7 +252,9 @@ bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_p
   const int64_t n_last = d.S - (int64_t)(d.nkb - 1) * g->k_block;
   a.ln_full = (float)std::log((double)g->k_block);
   a.ln_last = (float)std::log((double)n_last);
-  if (bsa::importance_lds_bytes(a) > 160 * 1024) return fail(BSA_ERR_UNSUPPORTED, "LDS budget exceeded");
+  a.G = bsa::importance_group(n_clusters, d.nkb, d.nqb);
+  a.area_a = 0;
+  if (bsa::importance_lds_bytes(a) > 96 * 1024) return fail(BSA_ERR_UNSUPPORTED, "LDS budget exceeded");
   hipError_t e = bsa::launch_importance(a, dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "importance launch: %s", hipGetErrorString(e));
   return ok();

@@ -98,6 +98,8 @@ struct ImpArgs {
   int32_t log_cluster;
   float ln_full;      // fp32(ln k_block)
   float ln_last;      // fp32(ln n_last)
+  int32_t G;          // query blocks per workgroup (importance_group)
+  int32_t area_a;     // floats of the shared token / logit area (set by the launcher)
 };
 
 // Launch arguments of the sparse forward kernel.
@@ -134,6 +136,7 @@ inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int
 
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
+int importance_group(int C, int nkb, int nqb);
 size_t importance_lds_bytes(const ImpArgs& a);
 int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb);
 hipError_t launch_topp(const TopPArgs& a, hipStream_t stream);

@@ -8,24 +8,27 @@
 // cluster-size-weighted softmax of a representative over the key-block
 // summaries is Eq. 2 (P') of "Competition Domains Matter ... (EG-Sparse)".
 //
-// One workgroup (4 waves) per (b, h, query block):
-//   1. the block's valid query tokens go to LDS as float32 (rows padded by
-//      one float, so a thread per token reads without bank conflicts);
-//   2. Lloyd k-means: centroid c starts at token floor(c n / C); each round
-//      assigns every token (one thread per (token, cluster) distance, a
-//      sequential non-fused chain over the channels; the lowest cluster
-//      among equals) and replaces every non-empty centroid by the mean of
-//      its tokens (one thread per (cluster, channel), ascending tokens); a
-//      final assignment gives the cluster sizes;
-//   3. logits of every centroid against every key-block summary (the same
-//      chain as the block logits of the mask), the summaries staged through
-//      LDS in chunks of 64 with coalesced loads, one thread per (key block,
-//      cluster);
-//   4. per non-empty cluster: row max, e = exp(z - max) by the fixed-order
-//      exponential, the sum by a halving tree over the row padded to a
-//      power of two (levels of 64 and more through LDS, the rest by lane
-//      shuffles inside one wave, the same pairs), p = e / sum; the importance
-//      accumulates fl32(w p) with w = m_c / n, clusters in ascending order.
+// One workgroup (8 waves) per G consecutive query blocks of one head, with
+// G * C <= 16 centroid rows:
+//   1. for each block in turn: its valid query tokens go to LDS as float32
+//      (rows padded by four floats, so a thread per token reads 16-byte
+//      chunks without bank conflicts), then Lloyd k-means: centroid c starts at token
+//      floor(c n / C); each round assigns every token (one thread per
+//      (token, cluster) distance, a sequential non-fused chain over the
+//      channels; the lowest cluster among equals) and replaces every
+//      non-empty centroid by the mean of its tokens (one thread per
+//      (cluster, channel), ascending tokens); a final assignment gives the
+//      cluster sizes;
+//   2. logits of every centroid of the group against every key-block summary
+//      (the same chain as the block logits of the mask): a thread owns all 16
+//      centroid rows x JT key blocks, so each summary read from L2 feeds 16
+//      chains and each centroid read is an LDS broadcast;
+//   3. per non-empty centroid row, one wave: row max, e = exp(z - max) by the
+//      fixed-order exponential, the sum by a halving tree over the row padded
+//      to a power of two (pairs k, k + h at every level; the levels of 64 and
+//      more inside each lane's registers, the rest by lane shuffles);
+//   4. the importance of every block: fl32(w p) with p = e / sum and
+//      w = m_c / n accumulated over its clusters in ascending order.
 // Every operation is a single float32 rounding in a fixed order, so the
 // importance (and the selection that ranks it) is reproducible bit for bit.
 #include "bsa_internal.h"
@@ -34,10 +37,11 @@
 namespace bsa {
 namespace {
 
-constexpr int kImpThreads = 256;
+constexpr int kImpThreads = 512;
+constexpr int kImpWaves = kImpThreads / 64;
 constexpr int kMaxClusters = 8;
-constexpr int kMaxOwned = 32;   // key blocks per thread: nkb <= 8192
-constexpr int kChunk = 64;      // key-block summaries per LDS chunk
+constexpr int kImpRows = 16;    // centroid rows of a workgroup
+constexpr int kImpZMax = 16384; // logits of a workgroup (G * C * nkb)
 
 template <typename T>
 __device__ __forceinline__ float widen(const T* p, int64_t e);
@@ -50,236 +54,307 @@ __device__ __forceinline__ float widen<float>(const float* p, int64_t e) {
   return p[e];
 }
 
-// floats of the area that holds the tokens, then the key-block chunks
-__host__ __device__ inline int tok_floats(int q_block, int D) {
-  const int t = q_block * (D + 1), k = kChunk * (D + 4);
-  return t > k ? t : k;
+// Sum of e_k = exp(z_k - mx) over a row of nkb logits by the halving tree
+// over the row padded to P (a power of two, P >= 2): level h adds k and
+// k + h for every k < h.  The first level computes the exponentials and
+// writes them back over the logits.  Lane l keeps the level-(P/2) values
+// k = l + 64 m (m < M) in registers, so every level h >= 64 stays inside the
+// lane; the levels below 64 go through lane shuffles.  Wave-uniform call.
+template <int M>
+__device__ float row_tree_sum(float* zr, int nkb, int P, float mx, int lane) {
+  const int h0 = P / 2;
+  float V[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int k = lane + 64 * m;
+    float v = 0.0f;
+    if (k < h0) {
+      const float e0 = k < nkb ? exp_le0(__fsub_rn(zr[k], mx)) : 0.0f;
+      const float e1 = k + h0 < nkb ? exp_le0(__fsub_rn(zr[k + h0], mx)) : 0.0f;
+      if (k < nkb) zr[k] = e0;
+      if (k + h0 < nkb) zr[k + h0] = e1;
+      v = __fadd_rn(e0, e1);
+    }
+    V[m] = v;
+  }
+#pragma unroll
+  for (int hh = M / 2; hh >= 1; hh >>= 1)
+#pragma unroll
+    for (int m = 0; m < hh; ++m) V[m] = __fadd_rn(V[m], V[m + hh]);
+  float v = V[0];
+  for (int h = (h0 < 64 ? h0 : 64) / 2; h >= 1; h >>= 1) {
+    const float o = __shfl_down(v, h, 64);
+    if (lane < h) v = __fadd_rn(v, o);
+  }
+  return __shfl(v, 0, 64);
 }
 
-template <typename T>
+template <typename T, int JT>
 __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  __shared__ __attribute__((aligned(16))) float mu_all[kImpRows * 128];   // centroids of the group, zero rows unused
+  __shared__ int msz_all[kImpRows];                   // cluster sizes (0: empty or c >= C_eff)
+  __shared__ int n_all[kImpRows];                     // valid tokens of each block
+  __shared__ float zsum[kImpRows];                    // row sums of e
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;                   // bh * nqb + i
-  const int bh = (int)(row / a.nqb);
-  const int i = (int)(row % a.nqb);
+  const int lane = tid & 63, wave = tid >> 6;
   const int D = a.D;
-  const int DP = D + 1;
+  const int DP = D + 4;                               // token row stride: 16-byte rows, no bank conflicts
   const int nkb = a.nkb;
-  const int64_t lo = (int64_t)i * a.q_block;
-  const int n = (int)min((int64_t)a.q_block, a.S - lo);
-  const int ce = min(a.C, n);
+  const int C = a.C;
+  const int ngroups = (a.nqb + a.G - 1) / a.G;
+  const int bh = blockIdx.x / ngroups;
+  const int i0 = (blockIdx.x % ngroups) * a.G;
+  const int nblk = min(a.G, a.nqb - i0);
 
-  float* xs = lds;                                   // [q_block][D + 1], later [kChunk][D + 4]
-  float* mu = xs + tok_floats(a.q_block, D);         // [C][D]
-  int* asg = reinterpret_cast<int*>(mu + a.C * D);   // [q_block]
-  int* msz = asg + a.q_block;                        // [8]
-  float* dist = reinterpret_cast<float*>(msz + kMaxClusters); // [C][q_block]
-  float* zb = dist + a.C * a.q_block;                // [C][nkb]
-  float* red = zb + a.C * nkb;                       // [max(256, P / 2)]
+  // area A: the tokens of one block during k-means, then the logit rows
+  float* xs = lds;                                    // [q_block][D + 4]
+  float* zs = lds;                                    // [G * C][nkb]
+  int* asg = reinterpret_cast<int*>(lds + a.area_a);  // [q_block]
+  float* dist = reinterpret_cast<float*>(asg + a.q_block);   // [C][q_block]
 
-  // ---- 1. tokens ----
-  const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)bh * a.seq_alloc + lo) * D;
-  for (int e = tid; e < n * D; e += kImpThreads) xs[(e / D) * DP + e % D] = widen(qb, e);
-  __syncthreads();
-  for (int e = tid; e < ce * D; e += kImpThreads) {
-    const int c = e / D, d = e % D;
-    mu[e] = xs[((c * n) / ce) * DP + d];
-  }
+  for (int e = tid; e < kImpRows * 128; e += kImpThreads) mu_all[e] = 0.0f;
+  if (tid < kImpRows) msz_all[tid] = 0;
   __syncthreads();
 
-  // ---- 2. k-means ----
-  // distance of every (token, cluster) pair by its own thread, then the
-  // nearest cluster of every token (lowest index among equals)
-  auto assign = [&]() {
-    for (int e = tid; e < n * ce; e += kImpThreads) {
-      const int t = e % n, c = e / n;
-      const float* xr = xs + t * DP;
-      const float* mr = mu + c * D;
-      float acc = 0.0f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) {
-        const float df = __fsub_rn(xr[d], mr[d]);
-        acc = __fadd_rn(acc, __fmul_rn(df, df));
-      }
-      dist[e] = acc;
-    }
+  // ---- 1. k-means of every block of the group, one block at a time ----
+  for (int g = 0; g < nblk; ++g) {
+    const int i = i0 + g;
+    const int64_t lo = (int64_t)i * a.q_block;
+    const int n = (int)min((int64_t)a.q_block, a.S - lo);
+    const int ce = min(C, n);
+    float* mu = mu_all + g * C * D;
+    const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)bh * a.seq_alloc + lo) * D;
+    for (int e = tid; e < n * D; e += kImpThreads) xs[(e / D) * DP + e % D] = widen(qb, e);
     __syncthreads();
-    for (int t = tid; t < n; t += kImpThreads) {
-      int best = 0;
-      float bd = dist[t];
-      for (int c = 1; c < ce; ++c) {
-        const float v = dist[c * n + t];
-        if (v < bd) {
-          bd = v;
-          best = c;
-        }
-      }
-      asg[t] = best;
-    }
-    __syncthreads();
-  };
-  for (int it = 0; it < a.T; ++it) {
-    assign();
     for (int e = tid; e < ce * D; e += kImpThreads) {
       const int c = e / D, d = e % D;
-      // members in ascending token order; a non-member adds +0, which leaves
-      // a nonzero sum unchanged and can only turn a -0 sum into +0 (the same
-      // distances and logits: both enter through x - mu and mu * k, and a
-      // zero logit is stored as +0)
-      float acc = 0.0f;
-      int m = 0;
+      mu[e] = xs[((c * n) / ce) * DP + d];
+    }
+    __syncthreads();
+    // distance of every (token, cluster) pair by its own thread, then the
+    // nearest cluster of every token (lowest index among equals); with one
+    // cluster every token is in it and no distance is needed
+    auto assign = [&]() {
+      if (ce == 1) {
+        for (int t = tid; t < n; t += kImpThreads) asg[t] = 0;
+        __syncthreads();
+        return;
+      }
+      for (int e = tid; e < n * ce; e += kImpThreads) {
+        const int t = e % n, c = e / n;
+        const float* xr = xs + t * DP;
+        const float* mr = mu + c * D;
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 4) {
+          const float4 x4 = *reinterpret_cast<const float4*>(xr + d);
+          const float4 m4 = *reinterpret_cast<const float4*>(mr + d);
+          float df = __fsub_rn(x4.x, m4.x);
+          acc = __fadd_rn(acc, __fmul_rn(df, df));
+          df = __fsub_rn(x4.y, m4.y);
+          acc = __fadd_rn(acc, __fmul_rn(df, df));
+          df = __fsub_rn(x4.z, m4.z);
+          acc = __fadd_rn(acc, __fmul_rn(df, df));
+          df = __fsub_rn(x4.w, m4.w);
+          acc = __fadd_rn(acc, __fmul_rn(df, df));
+        }
+        dist[e] = acc;
+      }
+      __syncthreads();
+      for (int t = tid; t < n; t += kImpThreads) {
+        int best = 0;
+        float bd = dist[t];
+        for (int c = 1; c < ce; ++c) {
+          const float v = dist[c * n + t];
+          if (v < bd) {
+            bd = v;
+            best = c;
+          }
+        }
+        asg[t] = best;
+      }
+      __syncthreads();
+    };
+    for (int it = 0; it < a.T; ++it) {
+      assign();
+      for (int e = tid; e < ce * D; e += kImpThreads) {
+        const int c = e / D, d = e % D;
+        // members in ascending token order; a non-member adds +0, which
+        // leaves a nonzero sum unchanged and can only turn a -0 sum into +0
+        // (the same distances and logits: both enter through x - mu and
+        // mu * k, and a zero logit is stored as +0)
+        float acc = 0.0f;
+        int m = 0;
 #pragma unroll 8
-      for (int t = 0; t < n; ++t) {
-        const bool in = asg[t] == c;
-        acc = __fadd_rn(acc, in ? xs[t * DP + d] : 0.0f);
-        m += in ? 1 : 0;
+        for (int t = 0; t < n; ++t) {
+          const bool in = asg[t] == c;
+          acc = __fadd_rn(acc, in ? xs[t * DP + d] : 0.0f);
+          m += in ? 1 : 0;
+        }
+        if (m > 0) mu[e] = __fdiv_rn(acc, (float)m);
       }
-      if (m > 0) mu[e] = __fdiv_rn(acc, (float)m);
+      __syncthreads();
     }
-    __syncthreads();
+    assign();
+    if (tid < ce) {
+      int m = 0;
+      for (int t = 0; t < n; ++t) m += asg[t] == tid ? 1 : 0;
+      msz_all[g * C + tid] = m;
+    }
+    if (tid == 0) n_all[g] = n;
+    __syncthreads();                                  // xs and asg are reused by the next block
   }
-  assign();
-  if (tid < ce) {
-    int m = 0;
-    for (int t = 0; t < n; ++t) m += asg[t] == tid ? 1 : 0;
-    msz[tid] = m;
+
+  // ---- 2. logits of every centroid row against every key-block summary ----
+  const int R = nblk * C;
+  const float* kbase = a.kp + (int64_t)bh * nkb * D;
+  for (int base = 0; base < nkb; base += kImpThreads * JT) {
+    float acc[kImpRows][JT];
+    const float* kr[JT];
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = min(base + tid + jj * kImpThreads, nkb - 1);
+      kr[jj] = kbase + (int64_t)j * D;
+#pragma unroll
+      for (int r = 0; r < kImpRows; ++r) acc[r][jj] = 0.0f;
+    }
+    for (int d = 0; d < D; d += 4) {
+      float4 kv[JT];
+#pragma unroll
+      for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
+#pragma unroll
+      for (int r = 0; r < kImpRows; ++r) {
+        const float4 m = *reinterpret_cast<const float4*>(mu_all + r * D + d);
+#pragma unroll
+        for (int jj = 0; jj < JT; ++jj) {
+          float t = acc[r][jj];
+          t = __fadd_rn(t, __fmul_rn(m.x, kv[jj].x));
+          t = __fadd_rn(t, __fmul_rn(m.y, kv[jj].y));
+          t = __fadd_rn(t, __fmul_rn(m.z, kv[jj].z));
+          t = __fadd_rn(t, __fmul_rn(m.w, kv[jj].w));
+          acc[r][jj] = t;
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = base + tid + jj * kImpThreads;
+      if (j < nkb) {
+        const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+        for (int r = 0; r < kImpRows; ++r) {
+          if (r < R) {
+            float z = __fmul_rn(acc[r][jj], a.scale);
+            if (a.log_cluster) z = __fadd_rn(z, lc);
+            if (z == 0.0f) z = 0.0f;                  // -0 -> +0
+            zs[r * nkb + j] = z;
+          }
+        }
+      }
+    }
   }
   __syncthreads();
 
-  // ---- 3. logits of every centroid against every key-block summary ----
-  // The summaries go through LDS (the token area, free by now) in chunks of
-  // kChunk rows with coalesced loads; one thread per (row of the chunk,
-  // cluster), threads of a wave on consecutive rows of one cluster.
-  const float* kb = a.kp + (int64_t)bh * nkb * D;
-  const int KS = D + 4;                              // padded row stride (16-byte rows)
-  float* ks = xs;
-  for (int j0 = 0; j0 < nkb; j0 += kChunk) {
-    const int nj = min(kChunk, nkb - j0);
-    __syncthreads();                                 // the previous chunk is consumed
-    const int D4 = D / 4;
-    for (int e = tid; e < nj * D4; e += kImpThreads) {
-      const int r = e / D4, c4 = e % D4;
-      *reinterpret_cast<float4*>(ks + r * KS + 4 * c4) =
-          *reinterpret_cast<const float4*>(kb + (int64_t)(j0 + r) * D + 4 * c4);
-    }
-    __syncthreads();
-    for (int e = tid; e < kChunk * ce; e += kImpThreads) {
-      const int jl = e % kChunk, c = e / kChunk;
-      if (jl >= nj) continue;
-      const float* kr = ks + jl * KS;
-      const float* mr = mu + c * D;
-      float acc = 0.0f;
-      for (int d = 0; d < D; d += 4) {
-        const float4 kv = *reinterpret_cast<const float4*>(kr + d);
-        const float4 m = *reinterpret_cast<const float4*>(mr + d);
-        acc = __fadd_rn(acc, __fmul_rn(m.x, kv.x));
-        acc = __fadd_rn(acc, __fmul_rn(m.y, kv.y));
-        acc = __fadd_rn(acc, __fmul_rn(m.z, kv.z));
-        acc = __fadd_rn(acc, __fmul_rn(m.w, kv.w));
-      }
-      const int j = j0 + jl;
-      const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
-      float z = __fmul_rn(acc, a.scale);
-      if (a.log_cluster) z = __fadd_rn(z, lc);
-      if (z == 0.0f) z = 0.0f;                      // -0 -> +0
-      zb[c * nkb + j] = z;
-    }
-  }
-  __syncthreads();
-
-  // ---- 4. softmax of every non-empty cluster, token-share-weighted sum ----
+  // ---- 3. softmax sums of every non-empty centroid row, one wave per row ----
   int P = 1;
   while (P < nkb) P <<= 1;
-  float imp[kMaxOwned];
+  for (int r = wave; r < R; r += kImpWaves) {
+    if (msz_all[r] == 0) continue;                    // uniform per wave
+    float* zr = zs + r * nkb;
+    float mx = -INFINITY;
+    for (int j = lane; j < nkb; j += 64) mx = fmaxf(mx, zr[j]);
 #pragma unroll
-  for (int r = 0; r < kMaxOwned; ++r) imp[r] = 0.0f;
-  for (int c = 0; c < ce; ++c) {
-    if (msz[c] == 0) continue;                       // uniform: msz is in LDS
-    float* zc = zb + c * nkb;
-    float m = -INFINITY;
-    for (int j = tid; j < nkb; j += kImpThreads) m = fmaxf(m, zc[j]);
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));   // max is exact in any order
-    __syncthreads();
-    for (int j = tid; j < nkb; j += kImpThreads) zc[j] = exp_le0(__fsub_rn(zc[j], M));
-    __syncthreads();
+    for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));   // max is exact in any order
     float Z;
     if (P == 1) {
-      Z = zc[0];
+      if (lane == 0) zr[0] = exp_le0(__fsub_rn(zr[0], mx));
+      Z = __shfl(exp_le0(__fsub_rn(mx, mx)), 0, 64);
     } else {
-      const int h0 = P / 2;
-      for (int k = tid; k < h0; k += kImpThreads) {
-        const float v0 = k < nkb ? zc[k] : 0.0f;
-        const float v1 = k + h0 < nkb ? zc[k + h0] : 0.0f;
-        red[k] = __fadd_rn(v0, v1);
+      switch (P <= 128 ? 1 : P / 128) {
+        case 1: Z = row_tree_sum<1>(zr, nkb, P, mx, lane); break;
+        case 2: Z = row_tree_sum<2>(zr, nkb, P, mx, lane); break;
+        case 4: Z = row_tree_sum<4>(zr, nkb, P, mx, lane); break;
+        case 8: Z = row_tree_sum<8>(zr, nkb, P, mx, lane); break;
+        case 16: Z = row_tree_sum<16>(zr, nkb, P, mx, lane); break;
+        case 32: Z = row_tree_sum<32>(zr, nkb, P, mx, lane); break;
+        default: Z = row_tree_sum<64>(zr, nkb, P, mx, lane); break;
       }
-      __syncthreads();
-      // halving levels across waves through LDS while more than 64 values
-      // remain, the rest inside wave 0 with the same pairs (lane k adds lane
-      // k + h)
-      int cnt = h0;
-      for (; cnt > 64; cnt >>= 1) {
-        const int h = cnt >> 1;
-        for (int k = tid; k < h; k += kImpThreads) red[k] = __fadd_rn(red[k], red[k + h]);
-        __syncthreads();
-      }
-      if (tid < 64) {
-        float v = tid < cnt ? red[tid] : 0.0f;
-        for (; cnt > 1; cnt >>= 1) {
-          const int h = cnt >> 1;
-          const float o = __shfl_down(v, h, 64);
-          if (tid < h) v = __fadd_rn(v, o);
-        }
-        if (tid == 0) red[0] = v;
-      }
-      __syncthreads();
-      Z = red[0];
     }
-    const float w = __fdiv_rn((float)msz[c], (float)n);
-#pragma unroll
-    for (int r = 0; r < kMaxOwned; ++r) {
-      const int j = tid + r * kImpThreads;
-      if (j < nkb) imp[r] = __fadd_rn(imp[r], __fmul_rn(w, __fdiv_rn(zc[j], Z)));
+    if (lane == 0) zsum[r] = Z;
+  }
+  __syncthreads();
+
+  // ---- 4. importance: token-share-weighted sum over the clusters ----
+  for (int e = tid; e < nblk * nkb; e += kImpThreads) {
+    const int g = e / nkb, j = e % nkb;
+    float imp = 0.0f;
+    for (int c = 0; c < C; ++c) {
+      const int r = g * C + c;
+      const int m = msz_all[r];
+      if (m == 0) continue;
+      const float w = __fdiv_rn((float)m, (float)n_all[g]);
+      imp = __fadd_rn(imp, __fmul_rn(w, __fdiv_rn(zs[r * nkb + j], zsum[r])));
     }
-    __syncthreads();                                 // red is reused by the next cluster
+    a.imp[((int64_t)bh * a.nqb + i0 + g) * nkb + j] = imp;
   }
-  float* out = a.imp + row * nkb;
-#pragma unroll
-  for (int r = 0; r < kMaxOwned; ++r) {
-    const int j = tid + r * kImpThreads;
-    if (j < nkb) out[j] = imp[r];
-  }
+}
+
+template <int JT>
+hipError_t launch_jt(const ImpArgs& a, int dtype, size_t lds, unsigned grid, hipStream_t stream) {
+  const void* f = dtype == 0 ? reinterpret_cast<const void*>(&importance_kernel<bf16_t, JT>)
+                             : reinterpret_cast<const void*>(&importance_kernel<float, JT>);
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (dtype == 0)
+    hipLaunchKernelGGL((importance_kernel<bf16_t, JT>), dim3(grid), dim3(kImpThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL((importance_kernel<float, JT>), dim3(grid), dim3(kImpThreads), lds, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-size_t importance_lds_bytes(const ImpArgs& a) {
-  int P = 1;
-  while (P < a.nkb) P <<= 1;
-  const size_t red = (size_t)(P / 2 > kImpThreads ? P / 2 : kImpThreads);
-  return sizeof(float) * ((size_t)tok_floats(a.q_block, a.D) + (size_t)a.C * a.D + (size_t)a.q_block +
-                          kMaxClusters + (size_t)a.C * a.q_block + (size_t)a.C * a.nkb + red);
+// Query blocks per workgroup: more blocks share each key-summary read, but
+// their k-means runs one block after another.  With one cluster k-means is
+// only the mean, so up to 16 blocks; with more clusters at most 4 (measured
+// on MI355X: C = 2 runs 10 % faster with 4 than with 8).
+int importance_group(int C, int nkb, int nqb) {
+  int g = kImpRows / C;
+  if (C > 1 && g > 4) g = 4;
+  const int zg = kImpZMax / (C * nkb);
+  if (zg < g) g = zg;
+  if (g > nqb) g = nqb;
+  return g < 1 ? 1 : g;
 }
 
-hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream) {
+size_t importance_lds_bytes(const ImpArgs& a) {
+  const size_t tok = (size_t)a.q_block * (a.D + 4);
+  const size_t z = (size_t)a.G * a.C * a.nkb;
+  const size_t area = tok > z ? tok : z;
+  return sizeof(float) * (area + (size_t)a.q_block + (size_t)a.C * a.q_block);
+}
+
+hipError_t launch_importance(const ImpArgs& a0, int dtype, hipStream_t stream) {
+  ImpArgs a = a0;
+  const size_t tok = (size_t)a.q_block * (a.D + 4);
+  const size_t z = (size_t)a.G * a.C * a.nkb;
+  a.area_a = (int32_t)(tok > z ? tok : z);
   const size_t lds = importance_lds_bytes(a);
-  const int64_t grid = (int64_t)a.BH * a.nqb;
-  if (dtype == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&importance_kernel<bf16_t>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(importance_kernel<bf16_t>, dim3((unsigned)grid), dim3(kImpThreads), lds, stream, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&importance_kernel<float>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(importance_kernel<float>, dim3((unsigned)grid), dim3(kImpThreads), lds, stream, a);
+  const unsigned grid = (unsigned)((int64_t)a.BH * ((a.nqb + a.G - 1) / a.G));
+  // key blocks per thread: the fewest passes x JT, ties to the larger JT
+  int best = 1;
+  int64_t cost = INT64_MAX;
+  for (int t : {1, 2, 4}) {
+    const int64_t c = (int64_t)((a.nkb + kImpThreads * t - 1) / (kImpThreads * t)) * t;
+    if (c <= cost) {
+      cost = c;
+      best = t;
+    }
   }
-  return hipGetLastError();
+  if (best == 4) return launch_jt<4>(a, dtype, lds, grid, stream);
+  if (best == 2) return launch_jt<2>(a, dtype, lds, grid, stream);
+  return launch_jt<1>(a, dtype, lds, grid, stream);
 }
 
 }  // namespace bsa
