@@ -42,6 +42,7 @@ constexpr int kImpWaves = kImpThreads / 64;
 constexpr int kMaxClusters = 8;
 constexpr int kImpRows = 16;    // centroid rows of a workgroup
 constexpr int kImpZMax = 16384; // logits of a workgroup (G * C * nkb)
+constexpr int kImpPrefetch = 64 * 128 / kImpThreads;   // token elements per thread (q_block * D <= 8192)
 
 template <typename T>
 __device__ __forceinline__ float widen(const T* p, int64_t e);
@@ -118,14 +119,34 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __syncthreads();
 
   // ---- 1. k-means of every block of the group, one block at a time ----
+  // The tokens of the next block are loaded into registers while this one
+  // is clustered (a thread holds elements tid + k * kImpThreads).
+  auto block_tokens = [&](int g) {
+    const int64_t lo = (int64_t)(i0 + g) * a.q_block;
+    return reinterpret_cast<const T*>(a.q) + ((int64_t)bh * a.seq_alloc + lo) * D;
+  };
+  auto block_n = [&](int g) { return (int)min((int64_t)a.q_block, a.S - (int64_t)(i0 + g) * a.q_block); };
+  float pre[kImpPrefetch];
+  auto prefetch = [&](int g) {
+    const T* qb = block_tokens(g);
+    const int ne = block_n(g) * D;
+#pragma unroll
+    for (int k = 0; k < kImpPrefetch; ++k) {
+      const int e = tid + k * kImpThreads;
+      pre[k] = e < ne ? widen(qb, e) : 0.0f;
+    }
+  };
+  prefetch(0);
   for (int g = 0; g < nblk; ++g) {
-    const int i = i0 + g;
-    const int64_t lo = (int64_t)i * a.q_block;
-    const int n = (int)min((int64_t)a.q_block, a.S - lo);
+    const int n = block_n(g);
     const int ce = min(C, n);
     float* mu = mu_all + g * C * D;
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)bh * a.seq_alloc + lo) * D;
-    for (int e = tid; e < n * D; e += kImpThreads) xs[(e / D) * DP + e % D] = widen(qb, e);
+#pragma unroll
+    for (int k = 0; k < kImpPrefetch; ++k) {
+      const int e = tid + k * kImpThreads;
+      if (e < n * D) xs[(e / D) * DP + e % D] = pre[k];
+    }
+    if (g + 1 < nblk) prefetch(g + 1);
     __syncthreads();
     for (int e = tid; e < ce * D; e += kImpThreads) {
       const int c = e / D, d = e % D;
