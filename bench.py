@@ -139,8 +139,8 @@ def cluster_selector_timing(bsa, w, g, p, qd, kp, C, T, nqb, nkb, stream, ev, re
         e[2].record(stream)
         ti.append(e)
     torch.cuda.synchronize()
-    imp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ti]))
-    sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ti]))
+    imp_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ti]))
+    sel_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ti]))
     n = w.q_block
     ops_row = (T + 1) * n * C * w.D * 3 + T * n * C * w.D + C * nkb * w.D * 2 + C * nkb * 30
     lane_ops = float(w.B * w.H * nqb) * ops_row
@@ -181,7 +181,7 @@ def top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, reps=20):
         e[1].record(stream)
         ts.append(e)
     torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ts]))
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in ts]))
     n = w.B * w.H * nqb * nkb
     kept = int(cnt.sum().item())
     byts = 7.0 * n * 4 + n + 4.0 * kept + w.B * w.H * nqb * 4
@@ -231,7 +231,7 @@ def structured_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, window=3,
         e[4].record(stream)
         ts.append(e)
     torch.cuda.synchronize()
-    fs_ms, ls_ms, fw_ms, fp_ms = (float(np.mean([e[k].elapsed_time(e[k + 1]) for e in ts])) for k in range(4))
+    fs_ms, ls_ms, fw_ms, fp_ms = (float(np.median([e[k].elapsed_time(e[k + 1]) for e in ts])) for k in range(4))
     kept = int(cnt.sum().item())
     # P' entries the frame-score kernel reads (integer geometry of the frame runs)
     tpf = w.latent_h * w.latent_w
@@ -337,8 +337,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = s0.elapsed_time(s1) / a.steps
-    pool_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in times]))
-    mask_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in times]))
+    pool_ms = float(np.median([e[0].elapsed_time(e[1]) for e in times]))
+    mask_ms = float(np.median([e[1].elapsed_time(e[2]) for e in times]))
     fwd_times = [e[2].elapsed_time(e[3]) for e in times]
     fwd_ms = float(np.median(fwd_times))           # ms per forward call: the median over the timed steps
     fwd_ms_mean = float(np.mean(fwd_times))        # the average launch duration, for the roofline
