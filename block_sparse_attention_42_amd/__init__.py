@@ -13,6 +13,12 @@ PyTorch fallback.
     kp = bsa_pool_blocks(k, g, g.k_block)
     mask, cnt, idx, logw = bsa_build_mask(qp, kp, g, MaskParams(keep_ratio=0.1))
     out, lse = bsa_forward(q, k, v, g, cnt, idx, logw)
+
+Other list producers for the same forward: bsa_cluster_importance +
+bsa_select_blocks (intra-block clustering), bsa_select_top_p (top-p over
+competition domains), bsa_frame_scores + bsa_classify_heads +
+bsa_structured_lists (per-head frame contexts; run the forward with
+launch_order="frame_runs" on these lists).
 """
 from __future__ import annotations
 
