@@ -13,11 +13,11 @@
 // -- the largest score T with mass(score >= T) >= ceil(p * mass(pool)) --
 // is found by a radix select over the scores' order keys with integer bin
 // masses (four 8-bit passes, integer atomics).  A per-row local domain finds
-// its T by a bitwise search inside one wave.  Every block with score >= T is
-// kept.
+// its T by the same radix select inside one wave, with the bins in that
+// wave's LDS.  Every block with score >= T is kept.
 //
 // Kernels, in launch order (grid-wide dependencies between them):
-//   tp_row_entropy    one workgroup per row: sum_j -P log(P + eps) (float64)
+//   tp_row_entropy    one wave per row: sum_j -P log(P + eps) (float64)
 //   tp_head_entropy   one workgroup per head: the mean over its rows
 //   tp_pools          one workgroup per batch element: median split, pool of
 //                     every head, pool state cleared
@@ -28,8 +28,10 @@
 //                     bin masses of 16 rows per workgroup, then per pool a
 //                     suffix scan picks the digit
 //   tp_select         one wave per row: threshold (the pool's, or its own
-//                     bitwise search), safeguard, frame-0 rows, text columns,
+//                     radix select), safeguard, frame-0 rows, text columns,
 //                     compaction
+#include <type_traits>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -87,24 +89,22 @@ __device__ __forceinline__ float score_of(const TopPArgs& a, const Ws& w, int bh
   return (a.value_aware && pooled) ? __fmul_rn(s, w.vnorm[(int64_t)bh * a.vstride + j]) : s;
 }
 
+// one wave per row
 __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a) {
-  __shared__ double red[kTpThreads];
   const Ws w = ws_of(a);
-  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
   const float* s = a.scores + row * a.nkb;
   const double eps = (double)a.eps;
   double acc = 0.0;
-  for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
+  for (int j = lane; j < a.nkb; j += 64) {
     const double p = (double)s[j];
     acc -= p * log(p + eps);
   }
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int h = kTpThreads / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) w.row_ent[row] = red[0];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) w.row_ent[row] = acc;
 }
 
 __global__ __launch_bounds__(kTpThreads) void tp_head_entropy(TopPArgs a) {
@@ -173,8 +173,24 @@ __global__ __launch_bounds__(kTpThreads) void tp_value_norm(TopPArgs a) {
   if (e >= (int64_t)a.BH * a.nkb) return;
   const int bh = (int)(e / a.nkb), j = (int)(e % a.nkb);
   const float* v = a.vp + e * a.D;
+  // the loads are independent (16 bytes each, all issued up front); the sum
+  // is the ascending-channel chain
   float acc = 0.0f;
-  for (int d = 0; d < a.D; ++d) acc = __fadd_rn(acc, __fmul_rn(v[d], v[d]));
+  auto chain = [&](auto dn) {
+    constexpr int DN = decltype(dn)::value;
+    float4 x[DN / 4];
+#pragma unroll
+    for (int c = 0; c < DN / 4; ++c) x[c] = *reinterpret_cast<const float4*>(v + 4 * c);
+#pragma unroll
+    for (int c = 0; c < DN / 4; ++c) {
+      acc = __fadd_rn(acc, __fmul_rn(x[c].x, x[c].x));
+      acc = __fadd_rn(acc, __fmul_rn(x[c].y, x[c].y));
+      acc = __fadd_rn(acc, __fmul_rn(x[c].z, x[c].z));
+      acc = __fadd_rn(acc, __fmul_rn(x[c].w, x[c].w));
+    }
+  };
+  if (a.D == 128) chain(std::integral_constant<int, 128>{});
+  else chain(std::integral_constant<int, 64>{});
   w.vnorm[(int64_t)bh * a.vstride + j] = __fsqrt_rn(acc);
 }
 
@@ -237,15 +253,29 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
   __syncthreads();
   const uint32_t prefix = w.ps[pid].prefix;
   const int i1 = min(i0 + kRowsPerHist, a.nqb);
+  // most scores share their leading digits: a thread adds up a run of equal
+  // digits itself and makes one LDS atomic per run (integer sums: exact in
+  // any order)
+  uint32_t cur = 256u;
+  unsigned long long acc = 0ull;
   for (int i = i0; i < i1; ++i) {
     const int64_t row = (int64_t)bh * a.nqb + i;
     for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
       const float s = score_of(a, w, bh, row, j, true);
       const uint32_t k = okey(s);
       const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u;
-      if (match) atomicAdd(&bins[(k >> shift) & 255u], fixed_mass(s));
+      if (match) {
+        const uint32_t b = (k >> shift) & 255u;
+        if (b != cur) {
+          if (acc) atomicAdd(&bins[cur], acc);
+          cur = b;
+          acc = 0ull;
+        }
+        acc += fixed_mass(s);
+      }
     }
   }
+  if (acc) atomicAdd(&bins[cur], acc);
   __syncthreads();
   const unsigned long long v = bins[threadIdx.x];
   if (v) atomicAdd(&w.ps[pid].bins[threadIdx.x], v);
@@ -278,13 +308,17 @@ __global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
   ps->bins[d] = 0ull;
 }
 
-__global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
-  const Ws w = ws_of(a);
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
-  const int bh = (int)(row / a.nqb);
-  const int i = (int)(row % a.nqb);
+// One row of tp_select with PER live slots per lane (64 * PER >= nkb).
+// LDS operations of one wave complete in order; this waits for them and keeps
+// the compiler from moving LDS accesses across it
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int PER>
+__device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, int i, int lane,
+                           unsigned long long* bins) {
   const int n = a.nkb;
   const int pid = w.pool[bh];
   const bool pooled = pid >= 0;
@@ -293,46 +327,99 @@ __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
   int32_t* irow = a.idx + row * n;
   const bool dense = a.frame0_first >= 0 && i >= a.frame0_first && i <= a.frame0_last;
 
-  float sc[kTpPerLane];
-  uint32_t key[kTpPerLane];
+  float sc[PER];
 #pragma unroll
-  for (int mm = 0; mm < kTpPerLane; ++mm) {
+  for (int mm = 0; mm < PER; ++mm) {
     const int j = lane + 64 * mm;
     sc[mm] = j < n ? score_of(a, w, bh, row, j, pooled) : 0.0f;
-    key[mm] = j < n ? okey(sc[mm]) : 0u;                     // 0: below every score's key
   }
+  // order key of slot mm; 0 (below every score's key) past the row
+  auto key = [&](int mm) { return lane + 64 * mm < n ? okey(sc[mm]) : 0u; };
   uint32_t T;
   if (pooled) {
     T = w.ps[pid].prefix;
   } else {
+    // the row's own threshold: a radix select over its order keys, four
+    // 8-bit digits, with integer bin masses in this wave's LDS bins (the
+    // same search as the pooled domains')
     unsigned long long tot = 0ull;
 #pragma unroll
-    for (int mm = 0; mm < kTpPerLane; ++mm)
+    for (int mm = 0; mm < PER; ++mm)
       if (lane + 64 * mm < n) tot += fixed_mass(sc[mm]);
     tot = wave_sum_u64(tot);
-    const unsigned long long target = (unsigned long long)ceil(a.top_p * (double)tot);
+    unsigned long long rem = (unsigned long long)ceil(a.top_p * (double)tot);
     T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      unsigned long long m = 0ull;
+    for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-      for (int mm = 0; mm < kTpPerLane; ++mm)
-        if (key[mm] >= cand) m += fixed_mass(sc[mm]);
-      m = wave_sum_u64(m);
-      if (m >= target) T = cand;
+      for (int b = 0; b < 4; ++b) bins[4 * lane + b] = 0ull;
+      wave_lds_sync();
+      // a lane adds up a run of equal digits itself and makes one atomic per run
+      uint32_t cur = 256u;
+      unsigned long long acc = 0ull;
+#pragma unroll
+      for (int mm = 0; mm < PER; ++mm) {
+        const bool match = lane + 64 * mm < n && (shift == 24 || ((key(mm) ^ T) >> (shift + 8)) == 0u);
+        if (match) {
+          const uint32_t b = (key(mm) >> shift) & 255u;
+          if (b != cur) {
+            if (acc) atomicAdd(&bins[cur], acc);
+            cur = b;
+            acc = 0ull;
+          }
+          acc += fixed_mass(sc[mm]);
+        }
+      }
+      if (acc) atomicAdd(&bins[cur], acc);
+      wave_lds_sync();
+      // suffix sums: lane l holds digits 4l .. 4l + 3
+      unsigned long long v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[b] = bins[4 * lane + b];
+      v[2] += v[3];
+      v[1] += v[2];
+      v[0] += v[1];
+      unsigned long long above = 0ull;                       // digits of the lanes above
+      unsigned long long x = v[0];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_down(x, o, 64);
+        if (lane + o < 64) {
+          above += y;
+          x += y;
+        }
+      }
+      // x: suffix from digit 4l on; above: from digit 4l + 4 on
+      int dig = -1;
+      unsigned long long past = 0ull;
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        const unsigned long long sb = v[b] + above;                        // digits >= 4l + b
+        const unsigned long long sn = (b == 3 ? 0ull : v[b + 1]) + above;  // digits >= 4l + b + 1
+        if (dig < 0 && sb >= rem && sn < rem) {
+          dig = 4 * lane + b;
+          past = sn;
+        }
+      }
+      const uint64_t who = __ballot(dig >= 0);
+      const int src = (int)__builtin_ctzll(who);
+      dig = __shfl(dig, src, 64);
+      past = __shfl(past, src, 64);
+      rem -= past;
+      T |= (uint32_t)dig << shift;
+      wave_lds_sync();                                       // the bins are cleared next
     }
   }
   // kept: score >= T; a pooled row left empty keeps its first largest block
   bool any = false;
 #pragma unroll
-  for (int mm = 0; mm < kTpPerLane; ++mm) any = any || (lane + 64 * mm < n && key[mm] >= T);
+  for (int mm = 0; mm < PER; ++mm) any = any || (lane + 64 * mm < n && key(mm) >= T);
   const bool row_empty = !__any(any);
   int safe = -1;
   if (pooled && row_empty) {
     float best = -1.0f;
     int bj = n;
 #pragma unroll
-    for (int mm = 0; mm < kTpPerLane; ++mm) {
+    for (int mm = 0; mm < PER; ++mm) {
       const int j = lane + 64 * mm;
       if (j < n && (sc[mm] > best || (sc[mm] == best && j < bj))) {
         best = sc[mm];
@@ -352,11 +439,11 @@ __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
   }
   int run = 0;
 #pragma unroll
-  for (int mm = 0; mm < kTpPerLane; ++mm) {
+  for (int mm = 0; mm < PER; ++mm) {
     const int j = lane + 64 * mm;
     if (64 * mm >= n) break;
     const bool in = j < n;
-    bool sel = in && (dense || key[mm] >= T || j == safe || j <= a.text_last);
+    bool sel = in && (dense || key(mm) >= T || j == safe || j <= a.text_last);
     const uint64_t bsel = __ballot(sel);
     const int pos = run + __popcll(bsel & below);
     if (in && mrow) mrow[j] = sel ? 1 : 0;
@@ -364,6 +451,20 @@ __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
     run += __popcll(bsel);
   }
   if (lane == 0) a.cnt[row] = run;
+}
+
+// PER: slots per lane, 64 * PER >= nkb (a kernel per PER, so each gets its
+// own register allocation)
+template <int PER>
+__global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
+  __shared__ unsigned long long sel_bins[256 * (kTpThreads / 64)];
+  const Ws w = ws_of(a);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
+  const int bh = (int)(row / a.nqb);
+  const int i = (int)(row % a.nqb);
+  select_row<PER>(a, w, bh, row, i, lane, sel_bins + 256 * (threadIdx.x >> 6));
 }
 
 }  // namespace
@@ -377,9 +478,8 @@ int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb) {
 }
 
 hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
-  const unsigned rows = (unsigned)((int64_t)a.BH * a.nqb);
   const unsigned wave_groups = (unsigned)(((int64_t)a.BH * a.nqb + 3) / 4);
-  hipLaunchKernelGGL(tp_row_entropy, dim3(rows), dim3(kTpThreads), 0, stream, a);
+  hipLaunchKernelGGL(tp_row_entropy, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
   hipLaunchKernelGGL(tp_head_entropy, dim3((unsigned)a.BH), dim3(kTpThreads), 0, stream, a);
   hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
   if (a.value_aware) {
@@ -396,7 +496,13 @@ hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(tp_digit, dim3((unsigned)a.npools), dim3(kTpThreads), 0, stream, a, shift);
     }
   }
-  hipLaunchKernelGGL(tp_select, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  const int per = (a.nkb + 63) / 64;
+  if (per <= 1) hipLaunchKernelGGL(tp_select<1>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  else if (per <= 2) hipLaunchKernelGGL(tp_select<2>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  else if (per <= 4) hipLaunchKernelGGL(tp_select<4>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  else if (per <= 8) hipLaunchKernelGGL(tp_select<8>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  else if (per <= 16) hipLaunchKernelGGL(tp_select<16>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  else hipLaunchKernelGGL(tp_select<kTpPerLane>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
   return hipGetLastError();
 }
 
