@@ -149,3 +149,35 @@ def test_cluster_importance_full_size_sampled_rows(name):
         assert cnt_h[b, h, i] == c and np.array_equal(idx_h[b, h, i, :c], oidx[b, h, i, :c]), (b, h, i)
     # every row sums to one within rounding (a property at any size)
     assert np.abs(imp_h.astype(np.float64).sum(-1) - 1.0).max() < 1e-5
+
+
+LONG_ROWS = {
+    # name: (workload, clusters, rounds); the row lengths take the register
+    # tree of 8, 32 and 64 values per lane, the last at C * nkb = 16384
+    "nkb1000_c4": (tiny(text_len=0, frames=4, lh=50, lw=80, bq=64, bk=16, D=64, H=1, dtype="bf16",
+                        mode="topk", topk=0, keep_ratio=0.05, centroids=16, grid=(4, 4), align=64), 4, 3),
+    "nkb3000_c4": (tiny(text_len=0, frames=6, lh=100, lw=80, bq=64, bk=16, D=64, H=1, dtype="bf16",
+                        mode="topk", topk=0, keep_ratio=0.05, centroids=16, grid=(4, 4), align=64), 4, 2),
+    "nkb8192_c2": (tiny(text_len=0, frames=8, lh=128, lw=128, bq=64, bk=16, D=64, H=1, dtype="bf16",
+                        mode="topk", topk=0, keep_ratio=0.01, centroids=16, grid=(4, 4), align=64), 2, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_ROWS))
+def test_cluster_importance_long_rows(name):
+    w, C, T = LONG_ROWS[name]
+    g = geometry_of(w)
+    _say(f"[gpu] cluster long rows {name} nkb={g.nkb} C={C} T={T}")
+    q, k, v = inputs_of(w)
+    gg = _geo(w)
+    qd, kd = _dev(w, q), _dev(w, k)
+    kp = bsa.bsa_pool_blocks(kd, gg, gg.k_block)
+    imp = bsa.bsa_cluster_importance(qd, kp, gg, C, T, w.log_cluster)
+    torch.cuda.synchronize()
+    imp_h = imp.cpu().numpy()
+    rows = [(0, 0, i) for i in (0, 1, g.nqb // 3, g.nqb // 2, g.nqb - 2, g.nqb - 1)]
+    okp = oracle.pool_blocks(k, g.S, g.k_block)
+    oimp = oracle.cluster_importance(q, okp, g, C, T, w.log_cluster, rows=rows)
+    for (b, h, i) in rows:
+        assert np.array_equal(imp_h[b, h, i], oimp[b, h, i]), (name, b, h, i)
+    assert np.abs(imp_h.astype(np.float64).sum(-1) - 1.0).max() < 1e-5

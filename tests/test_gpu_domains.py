@@ -128,3 +128,14 @@ def test_eg_routing_full_size():
     q, k, v = inputs_of(w)
     g, qd, kd, vd, P, vp = _scores(w, q, k, v)
     _check(w, P, vp, "eg", True, 0.9, frame0=True, text=False)
+
+
+@pytest.mark.parametrize("domain", ["row", "eg"])
+def test_max_row_length(domain):
+    """nkb = 2048, the limit of the top-p selector (32 slots per lane), every row."""
+    w = W.workload("wan_1p3b_sampled_k16").replace(H=2)
+    _say(f"[gpu] top-p nkb=2048 domain={domain}")
+    q, k, v = inputs_of(w)
+    g, qd, kd, vd, P, vp = _scores(w, q, k, v)
+    assert geometry_of(w).nkb == 2048
+    _check(w, P, vp, domain, True, 0.9, frame0=True, text=False)

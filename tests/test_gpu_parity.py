@@ -252,3 +252,25 @@ def test_deterministic_reruns():
     b = run_gpu(w, q, k, v)
     for key in ("qp", "kp", "mask", "cnt", "out", "lse", "logw"):
         assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_max_key_blocks():
+    """nkb = 8192, the limit of the top-k mask and the forward: the mask's LDS
+    radix select, frame-0 rows listing all 8192 blocks, 16-token key blocks.
+    Sampled rows (dense and sparse, first and last) against the oracle."""
+    w = tiny(text_len=0, frames=8, lh=128, lw=128, bq=64, bk=16, D=64, H=1, dtype="bf16", mode="topk",
+             topk=0, keep_ratio=0.01, frame0_dense=True, centroids=16, grid=(4, 4), align=64)
+    g = geometry_of(w)
+    assert g.nkb == 8192
+    q, k, v = inputs_of(w)
+    r = run_gpu(w, q, k, v)
+    oqp = oracle.pool_blocks(q, g.S, g.q_block)
+    okp = oracle.pool_blocks(k, g.S, g.k_block)
+    assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
+    f0 = list(g.frame0_q_blocks())
+    picks = [0, f0[-1], f0[-1] + 1, g.nqb // 2, g.nqb - 1]
+    rows = [(0, 0, i) for i in picks]
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w), rows=rows)
+    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    assert np.all(r["cnt"][0, 0, f0] == g.nkb)
+    _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, {(0, 0): picks})
