@@ -316,9 +316,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// The row's scores stay in registers (PER < 16) or in this wave's LDS
+// (srow, slot mm of lane l at mm * 64 + l): only the lane that wrote a slot
+// reads it, so the LDS copy needs no synchronization.
 template <int PER>
 __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, int i, int lane,
-                           unsigned long long* bins) {
+                           unsigned long long* bins, float* srow) {
+  constexpr bool kLds = PER >= 16;
   const int n = a.nkb;
   const int pid = w.pool[bh];
   const bool pooled = pid >= 0;
@@ -327,14 +331,20 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
   int32_t* irow = a.idx + row * n;
   const bool dense = a.frame0_first >= 0 && i >= a.frame0_first && i <= a.frame0_last;
 
-  float sc[PER];
+  float sreg[kLds ? 1 : PER];
 #pragma unroll
   for (int mm = 0; mm < PER; ++mm) {
     const int j = lane + 64 * mm;
-    sc[mm] = j < n ? score_of(a, w, bh, row, j, pooled) : 0.0f;
+    const float v = j < n ? score_of(a, w, bh, row, j, pooled) : 0.0f;
+    if constexpr (kLds) srow[mm * 64 + lane] = v;
+    else sreg[mm] = v;
   }
+  auto sc = [&](int mm) -> float {
+    if constexpr (kLds) return srow[mm * 64 + lane];
+    else return sreg[mm];
+  };
   // order key of slot mm; 0 (below every score's key) past the row
-  auto key = [&](int mm) { return lane + 64 * mm < n ? okey(sc[mm]) : 0u; };
+  auto key = [&](int mm) { return lane + 64 * mm < n ? okey(sc(mm)) : 0u; };
   uint32_t T;
   if (pooled) {
     T = w.ps[pid].prefix;
@@ -345,7 +355,7 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
     unsigned long long tot = 0ull;
 #pragma unroll
     for (int mm = 0; mm < PER; ++mm)
-      if (lane + 64 * mm < n) tot += fixed_mass(sc[mm]);
+      if (lane + 64 * mm < n) tot += fixed_mass(sc(mm));
     tot = wave_sum_u64(tot);
     unsigned long long rem = (unsigned long long)ceil(a.top_p * (double)tot);
     T = 0u;
@@ -366,7 +376,7 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
             cur = b;
             acc = 0ull;
           }
-          acc += fixed_mass(sc[mm]);
+          acc += fixed_mass(sc(mm));
         }
       }
       if (acc) atomicAdd(&bins[cur], acc);
@@ -421,8 +431,8 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
 #pragma unroll
     for (int mm = 0; mm < PER; ++mm) {
       const int j = lane + 64 * mm;
-      if (j < n && (sc[mm] > best || (sc[mm] == best && j < bj))) {
-        best = sc[mm];
+      if (j < n && (sc(mm) > best || (sc(mm) == best && j < bj))) {
+        best = sc(mm);
         bj = j;
       }
     }
@@ -458,13 +468,15 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
 template <int PER>
 __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
   __shared__ unsigned long long sel_bins[256 * (kTpThreads / 64)];
+  __shared__ float sel_rows[PER >= 16 ? 64 * PER * (kTpThreads / 64) : 1];
   const Ws w = ws_of(a);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
   if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
   const int bh = (int)(row / a.nqb);
   const int i = (int)(row % a.nqb);
-  select_row<PER>(a, w, bh, row, i, lane, sel_bins + 256 * (threadIdx.x >> 6));
+  select_row<PER>(a, w, bh, row, i, lane, sel_bins + 256 * (threadIdx.x >> 6),
+                  sel_rows + (PER >= 16 ? 64 * PER * (threadIdx.x >> 6) : 0));
 }
 
 }  // namespace
