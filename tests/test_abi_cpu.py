@@ -205,3 +205,16 @@ def test_head_labelling_on_the_host_matches_the_oracle():
     assert L.bsa_classify_heads(bad.ctypes.data, 1, 2, 1, np.zeros(2, np.int32).ctypes.data) == \
         _lib.BSA_ERR_INVALID_ARGUMENT
     assert b"finite" in L.bsa_last_error()
+
+
+def test_header_is_c99_and_a_c_client_links(tmp_path):
+    """include/bsa.h compiles as C99 with warnings as errors, and a plain C
+    client (tests/c_abi/bsa_example.c) links against libbsa.so; run without
+    arguments it prints its usage and touches no device."""
+    import subprocess
+    import __graft_entry__ as ge
+    out = str(tmp_path / "bsa_example")
+    r = subprocess.run(ge.c_example_cmd(ge.C_EXAMPLE_SRC, out), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([out], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
