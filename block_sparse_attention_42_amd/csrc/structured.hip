@@ -65,8 +65,12 @@ __global__ __launch_bounds__(kFsThreads) void frame_score_kernel(StructArgs a) {
     const float* p = a.scores + ((int64_t)bh * a.nqb + i) * a.nkb;
     const int nb = f - a.window + 1 > 1 ? f - a.window + 1 : 1;
     double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+    // ascending j in each run (unrolled so several loads are in flight)
+#pragma unroll 8
     for (int j = fb[0]; j < fb[1]; ++j) s0 += (double)p[j];
+#pragma unroll 8
     for (int j = fb[nb]; j < fb[f]; ++j) s1 += (double)p[j];
+#pragma unroll 8
     for (int j = fb[f]; j < fb[f + 1]; ++j) s2 += (double)p[j];
     const double s = s0 + s1 + s2;
     rows += 1.0;
