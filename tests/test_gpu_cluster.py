@@ -181,3 +181,25 @@ def test_cluster_importance_long_rows(name):
     for (b, h, i) in rows:
         assert np.array_equal(imp_h[b, h, i], oimp[b, h, i]), (name, b, h, i)
     assert np.abs(imp_h.astype(np.float64).sum(-1) - 1.0).max() < 1e-5
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_cluster_importance_random_geometries(k):
+    """Seeded random geometries, cluster counts and rounds: the importance of
+    every row bit-exact against the oracle."""
+    rng = np.random.default_rng(300 + k)
+    bq = int(rng.choice([32, 64]))
+    bk = int(rng.choice([16, 32, 64]))
+    D = int(rng.choice([64, 128]))
+    w = tiny(text_len=int(rng.integers(0, 60)), frames=int(rng.integers(1, 5)), lh=int(rng.integers(3, 12)),
+             lw=int(rng.integers(3, 14)), bq=bq, bk=bk, D=D, H=int(rng.integers(1, 4)), B=int(rng.integers(1, 3)),
+             dtype=str(rng.choice(["bf16", "f32"])), mode="topk", topk=0, keep_ratio=0.2,
+             log_cluster=bool(rng.integers(0, 2)), centroids=8, grid=(2, 4), align=max(bq, bk))
+    C, T = int(rng.integers(1, 9)), int(rng.integers(0, 5))
+    g = geometry_of(w)
+    _say(f"[gpu] cluster random #{k}: S={g.S} D={D} bq={bq} bk={bk} B={w.B} H={w.H} C={C} T={T} {w.dtype}")
+    q, kk, v = inputs_of(w)
+    r = _run(w, C, T, q, kk, v)
+    okp = oracle.pool_blocks(kk, g.S, g.k_block)
+    oimp = oracle.cluster_importance(q, okp, g, C, T, w.log_cluster)
+    assert np.array_equal(r["imp"], oimp)

@@ -139,3 +139,22 @@ def test_max_row_length(domain):
     g, qd, kd, vd, P, vp = _scores(w, q, k, v)
     assert geometry_of(w).nkb == 2048
     _check(w, P, vp, domain, True, 0.9, frame0=True, text=False)
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_domains_random_geometries(k):
+    """Seeded random geometries and top-p values, every domain: masks and
+    lists bit-exact against the oracle."""
+    rng = np.random.default_rng(100 + k)
+    bq = int(rng.choice([32, 64]))
+    bk = int(rng.choice([16, 32, 64]))
+    w = tiny(text_len=int(rng.integers(0, 60)), frames=int(rng.integers(2, 6)), lh=int(rng.integers(4, 12)),
+             lw=int(rng.integers(4, 14)), bq=bq, bk=bk, D=64, H=int(rng.integers(2, 6)), B=int(rng.integers(1, 3)),
+             dtype="bf16", mode="topk", topk=0, keep_ratio=0.2, centroids=8, grid=(2, 4), align=max(bq, bk))
+    p = float(rng.uniform(0.5, 0.99))
+    _say(f"[gpu] top-p random #{k}: S={geometry_of(w).S} bq={bq} bk={bk} B={w.B} H={w.H} p={p:.3f}")
+    q, k_, v = inputs_of(w)
+    g, qd, kd, vd, P, vp = _scores(w, q, k_, v)
+    for domain in ("row", "head", "split", "all", "eg"):
+        _check(w, P, vp, domain, bool(rng.integers(0, 2)), p, frame0=bool(rng.integers(0, 2)),
+               text=bool(rng.integers(0, 2)))

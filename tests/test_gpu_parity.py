@@ -274,3 +274,31 @@ def test_max_key_blocks():
     _check_lists(w, r, om, ocnt, oidx, ologw, rows)
     assert np.all(r["cnt"][0, 0, f0] == g.nkb)
     _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, {(0, 0): picks})
+
+
+@pytest.mark.parametrize("k", range(10))
+def test_random_geometries_every_row(k):
+    """Seeded random geometries, modes and options through the whole path:
+    pooled means, masks and lists bit-exact, outputs within tolerance, every row."""
+    rng = np.random.default_rng(500 + k)
+    bq = int(rng.choice([32, 64]))
+    bk = int(rng.choice([16, 32, 64]))
+    D = int(rng.choice([64, 128]))
+    mode = str(rng.choice(["topk", "sample"]))
+    w = tiny(text_len=int(rng.integers(0, 80)), frames=int(rng.integers(1, 6)), lh=int(rng.integers(2, 12)),
+             lw=int(rng.integers(2, 14)), bq=bq, bk=bk, D=D, H=int(rng.integers(1, 4)), B=int(rng.integers(1, 3)),
+             dtype=str(rng.choice(["bf16", "f32"])), mode=mode, topk=int(rng.integers(0, 4)),
+             keep_ratio=float(rng.uniform(0.05, 0.6)), frame0_dense=bool(rng.integers(0, 2)),
+             text_columns=bool(rng.integers(0, 2)), log_cluster=bool(rng.integers(0, 2)),
+             sample_seed=int(rng.integers(0, 1000)), centroids=8, grid=(2, 4), align=max(bq, bk))
+    g = geometry_of(w)
+    q, k_, v = inputs_of(w, pad_value=np.nan)
+    r = run_gpu(w, q, k_, v)
+    oqp = oracle.pool_blocks(q, g.S, g.q_block)
+    okp = oracle.pool_blocks(k_, g.S, g.k_block)
+    assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w))
+    rows = [(b, h, i) for b in range(g.B) for h in range(g.H) for i in range(g.nqb)]
+    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    _check_out(w, r, q, k_, v, g, ocnt, oidx, ologw,
+               {(b, h): list(range(g.nqb)) for b in range(g.B) for h in range(g.H)})

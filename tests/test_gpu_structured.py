@@ -177,3 +177,29 @@ def test_launch_orders_give_identical_outputs(name):
         assert torch.equal(o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1,
                            o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2)
         assert torch.equal(l1, l2)
+
+
+def _random_geometries(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bq = int(rng.choice([32, 64]))
+        bk = int(rng.choice([16, 32, 64]))
+        out.append(tiny(text_len=int(rng.integers(0, 90)), frames=int(rng.integers(1, 8)),
+                        lh=int(rng.integers(1, 12)), lw=int(rng.integers(1, 14)), bq=bq, bk=bk, D=64,
+                        H=int(rng.integers(1, 6)), B=int(rng.integers(1, 3)), dtype="bf16", align=max(bq, bk)))
+    return out
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_lists_random_geometries(k):
+    """Seeded random geometries (text, frames and latent sizes, block sizes),
+    random classes and options: lists bit-exact against the oracle."""
+    w = _random_geometries(2026, 12)[k]
+    rng = np.random.default_rng(k)
+    cls = rng.integers(0, 4, size=(w.B, w.H)).astype(np.int32)
+    window = int(rng.integers(1, 5))
+    prev, causal, f0, text = (bool(x) for x in rng.integers(0, 2, 4))
+    _say(f"[gpu] structured random #{k}: text={w.text_len} frames={w.frames} {w.latent_h}x{w.latent_w} "
+         f"bq={w.q_block} bk={w.k_block} B={w.B} H={w.H} L={window}")
+    _compare(w, cls, window, prev, causal, f0, text)
