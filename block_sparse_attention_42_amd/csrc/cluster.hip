@@ -39,7 +39,6 @@ namespace {
 
 constexpr int kImpThreads = 512;
 constexpr int kImpWaves = kImpThreads / 64;
-constexpr int kMaxClusters = 8;
 constexpr int kImpRows = 16;    // centroid rows of a workgroup
 constexpr int kImpZMax = 16384; // logits of a workgroup (G * C * nkb)
 constexpr int kImpPrefetch = 64 * 128 / kImpThreads;   // token elements per thread (q_block * D <= 8192)

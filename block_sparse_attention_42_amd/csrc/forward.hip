@@ -75,7 +75,6 @@ struct Row8;
 
 template <>
 struct Row8<bf16_t> {
-  static constexpr int kOps = 1;   // buffer loads per 8 elements
   static __device__ __forceinline__ uint4 ld(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
   static __device__ __forceinline__ uint4 buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
@@ -85,7 +84,6 @@ struct Row8<bf16_t> {
 
 template <>
 struct Row8<float> {
-  static constexpr int kOps = 2;
   static __device__ __forceinline__ uint4 ld(const float* p) {
     const float4 x = reinterpret_cast<const float4*>(p)[0];
     const float4 y = reinterpret_cast<const float4*>(p)[1];
@@ -659,7 +657,7 @@ void fwd_kernel(FwdArgs a) {
     //            MFMAs, the row max of S(u+1) between the second half's; the
     //            K(u+3) loads go in between, V fragments are read two ahead,
     //            and the K(u+2) fragments for the next step are read last.
-    auto step_mma = [&](auto par, int u, const Info& i_u3) {
+    auto step_mma = [&](auto par, const Info& i_u3) {
       constexpr int p = decltype(par)::value;   // u & 1
       f32x16 (&scur)[QT] = sc[p];
       f32x16 (&snext)[QT] = sc[p ^ 1];
@@ -849,7 +847,7 @@ void fwd_kernel(FwdArgs a) {
       if constexpr (kPair && p == 0) r5 = r4;
       else r5 = fetch(u + 5);
       if constexpr (kDma) {
-        step_mma(par, u, i_u3);
+        step_mma(par, i_u3);
       } else {
         load_tile(rv, i_u1, vslot(p ^ 1), false, full);
         bf16x8 pb[QT][2];
