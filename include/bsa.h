@@ -76,7 +76,11 @@ typedef enum { BSA_SELECT_TOPK = 0, BSA_SELECT_SAMPLE = 1 } bsa_select_mode;
  * latent_W tokens per frame, q_block_size; plus batch, heads, head_dim, the
  * key block size and the padded row count of every [B,H,seq_alloc,D] buffer.
  * Supported: head_dim 64 or 128; q_block 32 or 64; k_block 16, 32 or 64;
- * seq_alloc >= max(nqb*q_block, nkb*k_block). */
+ * seq_alloc >= max(nqb*q_block, nkb*k_block).
+ * Every entry point checks its geometry first: a NULL geometry, B or H < 1,
+ * a negative size, S < 1 or a short seq_alloc give BSA_ERR_INVALID_ARGUMENT;
+ * an unsupported head_dim, q_block or k_block, B*H > 2^24 or more than 2^30
+ * blocks give BSA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t B, H;
   int32_t text_len, frames, latent_h, latent_w;
@@ -116,7 +120,9 @@ typedef struct {
 } bsa_mask_params;
 
 /* Derived sizes of a geometry (host only, no device work).  `p` may be NULL,
- * then topk and expected are 0. */
+ * then topk and expected are 0.  Errors: the geometry checks; a NULL `out`;
+ * with `p`, an unknown mode, topk < 0 or keep_ratio outside (0, 1]
+ * (BSA_ERR_INVALID_ARGUMENT). */
 typedef struct {
   int64_t S;
   int32_t nqb, nkb;
@@ -136,7 +142,9 @@ bsa_status bsa_derive(const bsa_geometry* g, const bsa_mask_params* p, bsa_deriv
  *   pooled: [B, H, ceil(S/block), D] float32, written.  For block i with
  *           n = min(block, S - i*block) rows and channel d:
  *           acc = 0; for t ascending: acc = fl32(acc + x[t][d]);
- *           pooled = fl32(acc / n).  Bit-reproducible. */
+ *           pooled = fl32(acc / n).  Bit-reproducible.
+ *   Errors: an unknown dtype, `block` other than q_block or k_block, NULL or
+ *   misaligned buffers (BSA_ERR_INVALID_ARGUMENT, before any launch). */
 bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, int32_t block,
                            float* pooled, void* stream);
 
@@ -155,7 +163,10 @@ bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, 
  *   log_w:  [B, H, nqb, nkb] float32 or NULL (required for SAMPLE): the
  *           log-weight of list slot p of each row, 0 for top-k rows.
  *   nkb is limited to 8192 for top-k and 2048 for sampling
- *   (BSA_ERR_UNSUPPORTED beyond). */
+ *   (BSA_ERR_UNSUPPORTED beyond).
+ *   Errors: the parameter checks of bsa_derive; NULL q_pooled, k_pooled,
+ *   kv_cnt or kv_idx, a misaligned buffer, or SAMPLE without log_w
+ *   (BSA_ERR_INVALID_ARGUMENT, before any launch). */
 bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bsa_geometry* g,
                           const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
                           int32_t* kv_idx, float* log_w, void* stream);
@@ -178,7 +189,10 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
  *   lse:     NULL or [B, H, seq_alloc] float32, ln sum_u exp(logit_u);
  *            -inf for rows >= S and empty rows.
  *   Limits: nkb <= 8192 and one head of q/k/v below 2 GiB
- *   (BSA_ERR_UNSUPPORTED beyond). */
+ *   (BSA_ERR_UNSUPPORTED beyond).
+ *   Errors: an unknown dtype, NULL q, k, v, kv_cnt, kv_idx or out, a
+ *   misaligned buffer, or a softmax_scale that is negative or not finite
+ *   (BSA_ERR_INVALID_ARGUMENT, before any launch). */
 bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtype,
                        const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
                        const float* log_w, float softmax_scale, void* out, float* lse,
@@ -233,7 +247,9 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t d
  *   of fl32(fl32(m_c / n) * P_c,j): the expected attention mass a query of
  *   the block puts on key block j.  Bit-reproducible; each row sums to 1
  *   within rounding.  With C = 1 and T >= 1 it is P' of the pooled block.
- *   Limits: C * nkb <= 16384 and nkb <= 8192 (BSA_ERR_UNSUPPORTED beyond). */
+ *   Limits: C * nkb <= 16384 and nkb <= 8192 (BSA_ERR_UNSUPPORTED beyond).
+ *   Errors: an unknown dtype, NULL or misaligned buffers, C or T out of
+ *   range (BSA_ERR_INVALID_ARGUMENT, before any launch). */
 bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_pooled,
                                   const bsa_geometry* g, int32_t n_clusters, int32_t iters,
                                   int32_t log_cluster, float* importance, void* stream);
@@ -252,7 +268,8 @@ bsa_status bsa_cluster_importance(const void* q, int32_t dtype, const float* k_p
  *               from exp(z - max z); the safeguard keeps the first block of
  *               largest importance.
  *   mask, kv_cnt, kv_idx, log_w: as for bsa_build_mask.
- *   Limits as for bsa_build_mask. */
+ *   Limits and errors as for bsa_build_mask (with importance in place of
+ *   q_pooled and k_pooled). */
 bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g,
                              const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
                              int32_t* kv_idx, float* log_w, void* stream);
@@ -279,7 +296,8 @@ typedef struct {
   int32_t reserved;
 } bsa_topp_params;
 
-/* Bytes of device workspace bsa_select_top_p needs for this geometry. */
+/* Bytes of device workspace bsa_select_top_p needs for this geometry.
+ * Errors: the geometry checks; a NULL `bytes` (BSA_ERR_INVALID_ARGUMENT). */
 bsa_status bsa_top_p_workspace_bytes(const bsa_geometry* g, int64_t* bytes);
 
 /*   scores:      [B, H, nqb, nkb] float32 P' (finite, >= 0, each row of mass
@@ -297,8 +315,14 @@ bsa_status bsa_top_p_workspace_bytes(const bsa_geometry* g, int64_t* bytes);
  * split puts the floor(H/2) lowest-entropy heads of each batch element
  * (lower head first among equals) in the low group.  In a pooled domain a
  * row left empty keeps its first block of largest score.  Frame-0 rows and
- * text columns are applied after.  Limits: nkb <= 2048 (BSA_ERR_UNSUPPORTED
- * beyond); pooled value-aware scores should stay below 2^16. */
+ * text columns are applied after.  Limits: nkb <= 2048 and H <= 4096
+ * (BSA_ERR_UNSUPPORTED beyond); pooled value-aware scores should stay below
+ * 2^16.
+ * Errors: NULL params, an unknown domain, top_p outside (0, 1], an
+ * entropy_eps that is not finite and > 0, NULL scores, workspace, kv_cnt or
+ * kv_idx, value_aware without v_pooled, a misaligned buffer, or a workspace
+ * smaller than bsa_top_p_workspace_bytes (BSA_ERR_INVALID_ARGUMENT, before
+ * any launch). */
 bsa_status bsa_select_top_p(const float* scores, const float* v_pooled, const bsa_geometry* g,
                             const bsa_topp_params* tp, double* head_entropy, void* workspace,
                             int64_t workspace_bytes, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx,
