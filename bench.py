@@ -50,12 +50,15 @@ def _args():
 
 
 def code_digest(path_src):
-    """sha256 of a HIP source with `//` comments and blank lines removed (the code the counters measured)."""
+    """sha256 of a HIP source with `//` comments and blank lines removed, plus
+    its compile flags (the code the counters measured)."""
+    from block_sparse_attention_42_amd.build import COMMON, EXTRA
     out = []
     for line in open(path_src, encoding="utf-8"):
         code = line.split("//", 1)[0].rstrip()
         if code:
             out.append(code)
+    out.append(" ".join(COMMON + EXTRA.get(os.path.basename(path_src), [])))
     return hashlib.sha256("\n".join(out).encode()).hexdigest()
 
 

@@ -22,7 +22,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Pooling and mask decisions follow a written-out float32 operation order:
 # no contraction into fused multiply-adds anywhere in those files.
-EXTRA = {"pool.hip": ["-ffp-contract=off"], "mask.hip": ["-ffp-contract=off"],
+# The forward's hand-ordered pipeline schedules best with the ILP-maximizing
+# machine scheduler (measured on MI355X: 1-2.5 % faster than the default).
+EXTRA = {"forward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+         "pool.hip": ["-ffp-contract=off"], "mask.hip": ["-ffp-contract=off"],
          "cluster.hip": ["-ffp-contract=off"], "topp.hip": ["-ffp-contract=off"],
          "abi.cpp": ["-x", "hip", "-ffp-contract=off"]}
 
