@@ -73,6 +73,18 @@ def _traffic(path_src, name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _mfma_busy(path_src, name):
+    """The forward's matrix-core busy fraction from the committed rocprofv3 SQ
+    counters, if the kernel code is unchanged."""
+    f = os.path.join(ROOT, "profiles", f"sq_fwd_{name}.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    if rec.get("forward_hip_code_sha256") != code_digest(path_src):
+        return None
+    return rec.get("mfma_busy_frac")
+
+
 def cpu_baseline(w, q, k, v, nblocks, nheads):
     """The oracle, as it stands, on the first `nheads` heads: per head, pooling
     and the mask of every row, then token-expanded attention of `nblocks`
@@ -350,7 +362,9 @@ def main():
     value = flops / (step_ms * 1e-3) / 1e12
     pool_bytes = 2 * w.B * w.H * w.S * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (nqb + nkb) * w.D * 4
 
-    traffic = _traffic(os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", "forward.hip"), w.name)
+    fwd_src = os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", "forward.hip")
+    traffic = _traffic(fwd_src, w.name)
+    mfma_busy = _mfma_busy(fwd_src, w.name)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -380,7 +394,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(fwd_tflops_avg, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops_avg / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                     "frac": round(fwd_tflops_avg / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "mfma_busy": mfma_busy},
     }
     if a.cluster_clusters > 0 and a.cluster_clusters * nkb <= 16384:
         res["cluster_selector"] = cluster_selector_timing(bsa, w, g, p, qd, kp, a.cluster_clusters,
