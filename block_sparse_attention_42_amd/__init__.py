@@ -32,7 +32,7 @@ from . import _lib
 from ._lib import BsaError
 
 __all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
-           "bsa_build_mask", "bsa_forward", "bsa_cluster_importance", "bsa_select_blocks",
+           "bsa_build_mask", "bsa_forward", "bsa_forward_ex", "bsa_cluster_importance", "bsa_select_blocks",
            "bsa_select_top_p", "DOMAINS", "HEAD_CLASSES", "LAUNCH_ORDERS", "bsa_frame_scores", "bsa_classify_heads",
            "bsa_structured_lists", "library_path"]
 
@@ -289,7 +289,7 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
                 kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = False, launch_order: str = "frame_position",
-                stream=None):
+                stream=None, _ex: bool = False):
     """Attention of every query block over its listed key blocks.  Returns (out, lse or None).
 
     ``launch_order`` ("frame_position" or "frame_runs", see LAUNCH_ORDERS) only
@@ -316,9 +316,19 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
         _need(lse, "lse", (g.B, g.H, g.seq_alloc), torch.float32, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()), _ptr(kv_cnt), _ptr(kv_idx),
             _ptr(log_w), ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse))
-    if launch_order == "frame_position":
+    if launch_order == "frame_position" and not _ex:
         _lib.check(_lib.lib().bsa_forward(*args, _stream(stream)))
     else:
         opt = _lib.bsa_forward_options(LAUNCH_ORDERS[launch_order])
         _lib.check(_lib.lib().bsa_forward_ex(*args, ctypes.byref(opt), _stream(stream)))
     return out, lse
+
+
+def bsa_forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
+                   kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
+                   softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                   launch_order: str = "frame_position", stream=None):
+    """bsa_forward through the C entry point bsa_forward_ex (options: the launch order)."""
+    return bsa_forward(q, k, v, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, want_lse, launch_order, stream,
+                       _ex=True)

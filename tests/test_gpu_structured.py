@@ -173,7 +173,11 @@ def test_launch_orders_give_identical_outputs(name):
     for cnt, idx in ((c1, i1), (c2, i2)):
         o1, l1 = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, want_lse=True)
         o2, l2 = bsa.bsa_forward(qd, kd, vd, g, cnt, idx, None, want_lse=True, launch_order="frame_runs")
+        o3, l3 = bsa.bsa_forward_ex(qd, kd, vd, g, cnt, idx, None, want_lse=True)   # default order through _ex
         torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1,
+                           o3.view(torch.int16) if o3.dtype == torch.bfloat16 else o3)
+        assert torch.equal(l1, l3)
         assert torch.equal(o1.view(torch.int16) if o1.dtype == torch.bfloat16 else o1,
                            o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2)
         assert torch.equal(l1, l2)
