@@ -173,6 +173,9 @@ __device__ __forceinline__ void topk_row(const float* zr, int n, int k, int text
 // JT: key blocks per thread in the logits phase (1, 2 or 4).
 template <int JT>
 __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
+  // k chunks loaded together: a 64-byte run of each key row when JT = 4
+  // (measured 8-10 % faster there; with JT = 1 it is slower)
+  constexpr int KB = JT == 4 ? 4 : 1;
   __shared__ float zs[kZFloats];
   __shared__ float qs[kMaxRows * 128];
   __shared__ int hist_all[kMaskWaves * 256];
@@ -213,21 +216,26 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
 #pragma unroll
           for (int r = 0; r < kMaxRows; ++r) acc[r][jj] = 0.0f;
         }
-        for (int d = 0; d < D; d += 4) {
-          float4 kv[JT];
+        for (int d0 = 0; d0 < D; d0 += 4 * KB) {
+          float4 kv[KB][JT];
 #pragma unroll
-          for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
+          for (int b = 0; b < KB; ++b)
 #pragma unroll
-          for (int r = 0; r < kMaxRows; ++r) {
-            const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d);
+            for (int jj = 0; jj < JT; ++jj) kv[b][jj] = *reinterpret_cast<const float4*>(kr[jj] + d0 + 4 * b);
 #pragma unroll
-            for (int jj = 0; jj < JT; ++jj) {
-              float t = acc[r][jj];
-              t = __fadd_rn(t, __fmul_rn(qv.x, kv[jj].x));
-              t = __fadd_rn(t, __fmul_rn(qv.y, kv[jj].y));
-              t = __fadd_rn(t, __fmul_rn(qv.z, kv[jj].z));
-              t = __fadd_rn(t, __fmul_rn(qv.w, kv[jj].w));
-              acc[r][jj] = t;
+          for (int b = 0; b < KB; ++b) {
+#pragma unroll
+            for (int r = 0; r < kMaxRows; ++r) {
+              const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d0 + 4 * b);
+#pragma unroll
+              for (int jj = 0; jj < JT; ++jj) {
+                float t = acc[r][jj];
+                t = __fadd_rn(t, __fmul_rn(qv.x, kv[b][jj].x));
+                t = __fadd_rn(t, __fmul_rn(qv.y, kv[b][jj].y));
+                t = __fadd_rn(t, __fmul_rn(qv.z, kv[b][jj].z));
+                t = __fadd_rn(t, __fmul_rn(qv.w, kv[b][jj].w));
+                acc[r][jj] = t;
+              }
             }
           }
         }
@@ -438,7 +446,9 @@ hipError_t launch_mask(const MaskArgs& a, hipStream_t stream) {
   const int ngroups = (a.nqb + a.rows_per_group - 1) / a.rows_per_group;
   const int64_t grid = (int64_t)a.BH * ngroups;
   // key blocks per thread: the fewest passes x JT (per-lane work), ties to
-  // the larger JT (fewer q reads per product)
+  // the larger JT (fewer q reads per product).  Splitting a workgroup's rows
+  // over thread groups (fewer rows, more key blocks per thread) measured
+  // slower at every shape tried: it multiplies the scattered k reads.
   int jt = 1, best = 1 << 30;
   for (int t : {1, 2, 4}) {
     const int work = ((a.nkb + kMaskThreads * t - 1) / (kMaskThreads * t)) * t;
