@@ -31,6 +31,8 @@
 //      w = m_c / n accumulated over its clusters in ascending order.
 // Every operation is a single float32 rounding in a fixed order, so the
 // importance (and the selection that ranks it) is reproducible bit for bit.
+#include <atomic>
+
 #include "bsa_internal.h"
 #include "spec_math.h"
 
@@ -320,12 +322,29 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   }
 }
 
+// The dynamic LDS cap of each importance kernel is raised once per device to
+// the most any launch may ask for (the host refuses geometries needing more),
+// so later calls make no runtime call besides the launch: they can be
+// captured in a graph.
+constexpr int kImpLdsCap = 96 * 1024;
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_lds_cap_raised[kMaxDevices];   // per device: bit per (JT, dtype)
+
 template <int JT>
 hipError_t launch_jt(const ImpArgs& a, int dtype, size_t lds, unsigned grid, hipStream_t stream) {
   const void* f = dtype == 0 ? reinterpret_cast<const void*>(&importance_kernel<bf16_t, JT>)
                              : reinterpret_cast<const void*>(&importance_kernel<float, JT>);
-  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > (size_t)kImpLdsCap) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const uint32_t bit = 1u << (2 * (JT == 1 ? 0 : (JT == 2 ? 1 : 2)) + (dtype == 0 ? 0 : 1));
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (!known || !(g_lds_cap_raised[dev].load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kImpLdsCap);
+    if (e != hipSuccess) return e;
+    if (known) g_lds_cap_raised[dev].fetch_or(bit, std::memory_order_release);
+  }
   if (dtype == 0)
     hipLaunchKernelGGL((importance_kernel<bf16_t, JT>), dim3(grid), dim3(kImpThreads), lds, stream, a);
   else

@@ -47,8 +47,16 @@
  *     non-OK status means nothing was enqueued, except BSA_ERR_HIP from a
  *     failed launch.  bsa_last_error() gives a message (thread-local).  No
  *     C++ exception crosses this boundary and no call exits the process.
- *   - Entry points are reentrant; the only global state is the thread-local
- *     error message.
+ *   - Entry points are reentrant.  Global state: the thread-local error
+ *     message, and a per-device record that the importance kernels' dynamic
+ *     LDS limit has been raised (set by the first bsa_cluster_importance
+ *     call on each device).
+ *   - Stream capture: apart from that first bsa_cluster_importance call on a
+ *     device, an entry point makes no runtime call besides its kernel
+ *     launches (no memset, copy, allocation or synchronization), so any
+ *     sequence of calls on one stream can be captured in a HIP graph and
+ *     replayed; make the first bsa_cluster_importance call on a device
+ *     outside a capture.
  */
 #ifndef BSA_H
 #define BSA_H
