@@ -44,6 +44,7 @@ def _args():
     ap.add_argument("--cluster-iters", type=int, default=3)
     ap.add_argument("--no-top-p", action="store_true", help="skip the top-p domain selector timing")
     ap.add_argument("--no-structured", action="store_true", help="skip the structured-list producer timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the timing of the step replayed from a HIP graph")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -274,6 +275,35 @@ def structured_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, window=3,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def graph_timing(torch, step, stream, ev, steps, out):
+    """The same step captured once in a HIP graph and replayed: ms per replay,
+    and whether a replay rewrites the eager step's output bit for bit."""
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                            ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref))
+    s0, s1 = ev(), ev()
+    s0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    del graph
+    return {"ms_per_step": round(ms, 4), "replay_identical_to_eager": same}
+
+
 def main():
     a = _args()
     if a.calibrate_copy_mib:
@@ -397,6 +427,8 @@ def main():
                      "frac": round(fwd_tflops_avg / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "mfma_busy": mfma_busy},
     }
+    if not a.no_graph:
+        res["graph_step"] = graph_timing(torch, step, stream, ev, a.steps, out)
     if a.cluster_clusters > 0 and a.cluster_clusters * nkb <= 16384:
         res["cluster_selector"] = cluster_selector_timing(bsa, w, g, p, qd, kp, a.cluster_clusters,
                                                           a.cluster_iters, nqb, nkb, stream, ev)
