@@ -63,6 +63,10 @@ bsa_status check_geometry(const bsa_geometry* g, Derived* d) {
     return fail(BSA_ERR_INVALID_ARGUMENT, "seq_alloc %lld < %lld (blocks of the padded sequence)",
                 (long long)g->seq_alloc, (long long)need);
   if ((int64_t)g->B * g->H > (1 << 24)) return fail(BSA_ERR_UNSUPPORTED, "B*H too large");
+  // every launch covers at most B*H*max(nqb, nkb) block rows, counted in 32 bits
+  if ((int64_t)g->B * g->H * std::max(nqb, nkb) > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "B*H*max(nqb, nkb) = %lld block rows exceed one launch",
+                (long long)((int64_t)g->B * g->H * std::max(nqb, nkb)));
   d->S = S;
   d->nqb = (int32_t)nqb;
   d->nkb = (int32_t)nkb;

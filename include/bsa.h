@@ -87,8 +87,9 @@ typedef enum { BSA_SELECT_TOPK = 0, BSA_SELECT_SAMPLE = 1 } bsa_select_mode;
  * seq_alloc >= max(nqb*q_block, nkb*k_block).
  * Every entry point checks its geometry first: a NULL geometry, B or H < 1,
  * a negative size, S < 1 or a short seq_alloc give BSA_ERR_INVALID_ARGUMENT;
- * an unsupported head_dim, q_block or k_block, B*H > 2^24 or more than 2^30
- * blocks give BSA_ERR_UNSUPPORTED. */
+ * an unsupported head_dim, q_block or k_block, B*H > 2^24, more than 2^30
+ * blocks, or B*H*max(nqb, nkb) > 2^31 - 1 (the block rows of one launch)
+ * give BSA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t B, H;
   int32_t text_len, frames, latent_h, latent_w;

@@ -87,6 +87,12 @@ def test_validation_rejects_before_launch():
     assert L.bsa_forward(fake, fake, fake, 0, ctypes.byref(small), fake, fake, None, 0.0, fake, None,
                          None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert b"seq_alloc" in L.bsa_last_error()
+    # 4096 heads x 2^20 query blocks: more block rows than one launch counts
+    huge = _lib.bsa_geometry(1, 4096, 1 << 26, 0, 0, 0, 128, 64, 64, 0, 1 << 26)
+    assert L.bsa_pool_blocks(fake, 0, ctypes.byref(huge), 64, fake, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert b"block rows" in L.bsa_last_error()
+    assert L.bsa_build_mask(fake, fake, ctypes.byref(huge), ctypes.byref(p), fake, fake, fake, None,
+                            None) == _lib.BSA_ERR_UNSUPPORTED
     empty = _lib.bsa_geometry(1, 1, 0, 0, 4, 4, 64, 32, 32, 0, 64)
     assert L.bsa_derive(ctypes.byref(empty), None, ctypes.byref(_lib.bsa_derived())) == \
         _lib.BSA_ERR_INVALID_ARGUMENT
