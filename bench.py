@@ -391,6 +391,11 @@ def main():
     fwd_tflops_avg = flops / (fwd_ms_mean * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
     pool_bytes = 2 * w.B * w.H * w.S * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (nqb + nkb) * w.D * 4
+    # mask: the logits are D non-fused multiplies and D adds each (the VALU-bound part); its bytes are the
+    # pooled summaries in, and the mask, counts, listed indices (and log-weights) out
+    mask_lane_ops = 2.0 * w.B * w.H * nqb * nkb * w.D
+    mask_bytes = (w.B * w.H * (nqb + nkb) * w.D * 4 + w.B * w.H * nqb * nkb + w.B * w.H * nqb * 4
+                  + blocks * 4 * (2 if logw is not None else 1))
 
     fwd_src = os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", "forward.hip")
     traffic = _traffic(fwd_src, w.name)
@@ -419,6 +424,10 @@ def main():
         "pool_ms": round(pool_ms, 4),
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
         "mask_ms": round(mask_ms, 4),
+        "mask_gbs": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
+        "mask_valu": {"bound": "alu", "achieved": round(mask_lane_ops / (mask_ms * 1e-3) / 1e12, 2),
+                      "peak": round(PEAK_VALU_TLANEOPS, 2), "unit": "T lane-ops/s",
+                      "frac": round(mask_lane_ops / (mask_ms * 1e-3) / 1e12 / PEAK_VALU_TLANEOPS, 4)},
         "executed_blocks": blocks,
         "density": round(blocks / (w.B * w.H * nqb * nkb), 4),
         "wall_s_timed": round(wall, 3),
