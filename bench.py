@@ -45,6 +45,9 @@ def _args():
     ap.add_argument("--no-top-p", action="store_true", help="skip the top-p domain selector timing")
     ap.add_argument("--no-structured", action="store_true", help="skip the structured-list producer timing")
     ap.add_argument("--no-graph", action="store_true", help="skip the timing of the step replayed from a HIP graph")
+    ap.add_argument("--dense-split", default="auto",
+                    help="key split of the frame-0 rows in the forward: a number 1..16, or auto "
+                         "(suggest_dense_split from the lists, chosen before the timed steps)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -350,6 +353,8 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
 
+    split_box = [1, None]                 # dense_split, its workspace
+
     def step(times=None):
         e = [ev() for _ in range(4)] if times is not None else None
         if e: e[0].record(stream)
@@ -358,7 +363,7 @@ def main():
         if e: e[1].record(stream)
         bsa.bsa_build_mask(qp, kp, g, p, out=(mask, cnt, idx, logw))
         if e: e[2].record(stream)
-        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, out=out)
+        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, out=out, dense_split=split_box[0], workspace=split_box[1])
         if e:
             e[3].record(stream)
             times.append(e)
@@ -366,6 +371,14 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    # the key split of the frame-0 rows: chosen from the lists, outside the timed region
+    split = bsa.suggest_dense_split(g, cnt) if a.dense_split == "auto" else int(a.dense_split)
+    if split != 1:
+        split_box[:] = [split, torch.empty(max(bsa.bsa_forward_split_workspace_bytes(g, split), 16),
+                                           dtype=torch.uint8, device=dev)]
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
     blocks = int(cnt.sum().item())
     flops = 4.0 * w.D * w.q_block * w.k_block * blocks
 
@@ -416,7 +429,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "head_dim": w.D, "seq_len": w.S,
                    "seq_alloc": w.seq_alloc, "q_block": w.q_block, "k_block": w.k_block,
                    "selection": w.mode, "keep_ratio": w.keep_ratio, "frame0_dense": w.frame0_dense,
-                   "text_columns": w.text_columns},
+                   "text_columns": w.text_columns, "dense_split": split_box[0]},
         "fwd_ms_per_call": round(fwd_ms, 4),
         "fwd_ms_mean": round(fwd_ms_mean, 4),
         "fwd_tflops": round(fwd_tflops, 2),

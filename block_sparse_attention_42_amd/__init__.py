@@ -289,11 +289,15 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
                 kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = False, launch_order: str = "frame_position",
-                stream=None, _ex: bool = False):
+                stream=None, _ex: bool = False, dense_split: int = 1, workspace: Optional[torch.Tensor] = None):
     """Attention of every query block over its listed key blocks.  Returns (out, lse or None).
 
     ``launch_order`` ("frame_position" or "frame_runs", see LAUNCH_ORDERS) only
-    changes which work items run together; "frame_runs" calls bsa_forward_ex."""
+    changes which work items run together; "frame_runs" calls bsa_forward_ex.
+    ``dense_split`` > 1 splits each frame-0 row's list over that many work
+    items and merges their partial states (bsa_forward_split, with
+    ``workspace`` or a new one of bsa_forward_split_workspace_bytes bytes);
+    see suggest_dense_split."""
     if launch_order not in LAUNCH_ORDERS:
         raise ValueError(f"launch_order {launch_order!r} not in {sorted(LAUNCH_ORDERS)}")
     d = bsa_derive(g)
@@ -316,12 +320,51 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
         _need(lse, "lse", (g.B, g.H, g.seq_alloc), torch.float32, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()), _ptr(kv_cnt), _ptr(kv_idx),
             _ptr(log_w), ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse))
-    if launch_order == "frame_position" and not _ex:
+    if dense_split != 1:
+        nbytes = bsa_forward_split_workspace_bytes(g, dense_split)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+        opt = _lib.bsa_forward_options(LAUNCH_ORDERS[launch_order])
+        _lib.check(_lib.lib().bsa_forward_split(*args, ctypes.byref(opt), int(dense_split), _ptr(workspace),
+                                                workspace.numel(), _stream(stream)))
+    elif launch_order == "frame_position" and not _ex:
         _lib.check(_lib.lib().bsa_forward(*args, _stream(stream)))
     else:
         opt = _lib.bsa_forward_options(LAUNCH_ORDERS[launch_order])
         _lib.check(_lib.lib().bsa_forward_ex(*args, ctypes.byref(opt), _stream(stream)))
     return out, lse
+
+
+def bsa_forward_split_workspace_bytes(g: Geometry, dense_split: int) -> int:
+    """Bytes of workspace bsa_forward_split needs (0 when nothing is split)."""
+    nbytes = ctypes.c_int64(0)
+    _lib.check(_lib.lib().bsa_forward_split_workspace_bytes(ctypes.byref(g.c()), int(dense_split),
+                                                            ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def suggest_dense_split(g: Geometry, kv_cnt: torch.Tensor, simds: Optional[int] = None) -> int:
+    """A key split for the frame-0 rows from the lists' lengths (reads kv_cnt back: a synchronization).
+
+    A frame-0 row is walked by one wave; when it holds more blocks than the
+    launch's average per SIMD it becomes the launch's critical path.  The
+    split is that ratio, rounded, within 1..8, with at least 16 blocks a part
+    (shorter parts save less than the merge launch costs; measured on MI355X:
+    2 parts take the 122-block rows of a 5-frame Wan-like clip from 0.244 to
+    0.220 ms, while 7-block rows get slower)."""
+    d = bsa_derive(g)
+    if d["frame0_first"] < 0:
+        return 1
+    if simds is None:
+        simds = 4 * torch.cuda.get_device_properties(kv_cnt.device).multi_processor_count
+    cnt = kv_cnt.reshape(g.B * g.H, -1)
+    dense = cnt[:, d["frame0_first"]:d["frame0_last"] + 1]
+    longest = int(dense.max().item())
+    per_simd = float(cnt.sum().item()) / simds
+    if per_simd <= 0:
+        return 1
+    return int(max(1, min(8, longest // 16, round(longest / per_simd))))
 
 
 def bsa_forward_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,

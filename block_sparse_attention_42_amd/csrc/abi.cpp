@@ -472,10 +472,18 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, int32_t dtyp
   return bsa_forward_ex(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, nullptr, stream);
 }
 
-bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t dtype,
-                          const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
-                          const float* log_w, float softmax_scale, void* out, float* lse,
-                          const bsa_forward_options* opt, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// frame-0 query blocks of a derived geometry (the rows the forward runs first
+// and may split)
+int32_t dense_rows(const Derived& d) { return d.f0_first >= 0 ? d.f0_last - d.f0_first + 1 : 0; }
+
+bsa_status forward_impl(const void* q, const void* k, const void* v, int32_t dtype, const bsa_geometry* g,
+                        const int32_t* kv_cnt, const int32_t* kv_idx, const float* log_w, float softmax_scale,
+                        void* out, float* lse, const bsa_forward_options* opt, int32_t split, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
   const int32_t order = opt ? opt->launch_order : BSA_ORDER_FRAME_POSITION;
   if (order != BSA_ORDER_FRAME_POSITION && order != BSA_ORDER_FRAME_RUNS)
     return fail(BSA_ERR_INVALID_ARGUMENT, "unknown launch order %d", order);
@@ -518,8 +526,22 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t d
   a.dense_last = d.f0_last;
   const int64_t tpf = (int64_t)g->latent_h * g->latent_w;
   a.period = tpf > 0 ? (int32_t)std::max<int64_t>(1, (tpf + g->q_block / 2) / g->q_block) : 1;
-  const int32_t nd = d.f0_first >= 0 ? d.f0_last - d.f0_first + 1 : 0;
-  a.n_dense = a.BH * nd;
+  const int32_t nd = dense_rows(d);
+  if (split < 1 || split > 16) return fail(BSA_ERR_INVALID_ARGUMENT, "dense_split %d must be in 1..16", split);
+  if (nd == 0) split = 1;                        // no frame-0 rows: nothing to split
+  if (split > 1) {
+    const int64_t need = bsa::split_ws_floats((int64_t)a.BH * nd * split, g->q_block, g->head_dim) * 4;
+    if (!workspace || !aligned16(workspace))
+      return fail(BSA_ERR_INVALID_ARGUMENT, "the key split needs a 16-byte aligned workspace");
+    if (workspace_bytes < need)
+      return fail(BSA_ERR_INVALID_ARGUMENT, "workspace of %lld bytes < %lld needed", (long long)workspace_bytes,
+                  (long long)need);
+  }
+  if ((int64_t)a.BH * nd * split > 0x7fffffffLL)
+    return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+  a.split = split;
+  a.ws = split > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.n_dense = a.BH * nd * split;
   const int64_t n_other = (int64_t)a.BH * (d.nqb - nd);
   a.order = order;
   a.per_xcd = order == BSA_ORDER_FRAME_RUNS
@@ -529,6 +551,41 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t d
   hipError_t e = bsa::launch_forward(a, dtype, g->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t dtype,
+                          const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                          const float* log_w, float softmax_scale, void* out, float* lse,
+                          const bsa_forward_options* opt, void* stream) {
+  return forward_impl(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, opt, 1, nullptr, 0,
+                      stream);
+}
+
+bsa_status bsa_forward_split_workspace_bytes(const bsa_geometry* g, int32_t dense_split, int64_t* bytes) {
+  if (!bytes) return fail(BSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (dense_split < 1 || dense_split > 16)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "dense_split %d must be in 1..16", dense_split);
+  const int32_t nd = dense_rows(d);
+  *bytes = (dense_split > 1 && nd > 0)
+               ? bsa::split_ws_floats((int64_t)g->B * g->H * nd * dense_split, g->q_block, g->head_dim) * 4
+               : 0;
+  return ok();
+}
+
+bsa_status bsa_forward_split(const void* q, const void* k, const void* v, int32_t dtype,
+                             const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                             const float* log_w, float softmax_scale, void* out, float* lse,
+                             const bsa_forward_options* opt, int32_t dense_split, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return forward_impl(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, opt, dense_split,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -120,9 +120,21 @@ struct FwdArgs {
   int32_t dense_first, dense_last;   // frame-0 query blocks, run first (-1, -1: none)
   int32_t period;                    // query blocks per frame, rounded (>= 1)
   int32_t per_xcd;                   // remaining work items per XCD
-  int32_t n_dense;                   // BH * dense rows
+  int32_t n_dense;                   // dense work items: BH * dense rows * split
   int32_t order;                     // 0: frame-position runs, 1: frame runs of every head
+  // key split of the frame-0 rows (split > 1): work item t < n_dense covers
+  // part t % split of its row's list and leaves its partial softmax state in
+  // ws; a second kernel merges the parts into out and lse
+  int32_t split;                     // 1: off
+  float* ws;                         // partial states (split > 1), see split_ws_floats
 };
+
+// Workspace of the key split, in floats: per dense work item, the
+// unnormalized O rows (q_block x D), then the reference maxima (q_block, log2
+// domain) and the row sums (q_block) of all items.
+inline int64_t split_ws_floats(int64_t items, int32_t q_block, int32_t D) {
+  return items * q_block * (int64_t)D + 2 * items * q_block;
+}
 
 // Work items of the forward launch: the frame-0 (longest) rows of every head
 // first, dealt round-robin over the XCDs, then the other rows.  Order 0: in

@@ -174,8 +174,9 @@ __device__ __forceinline__ int swz_v(int r) {
 // blockIdx -> (head, query block); false for the few padding workgroups.
 __device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& qb) {
   if (t < a.n_dense) {
-    bh = t % a.BH;
-    qb = a.dense_first + t / a.BH;
+    const int r = t / a.split;                     // the split parts of a row are adjacent items
+    bh = r % a.BH;
+    qb = a.dense_first + r / a.BH;
     return true;
   }
   const int nd = a.dense_first >= 0 ? a.dense_last - a.dense_first + 1 : 0;
@@ -248,7 +249,12 @@ void fwd_kernel(FwdArgs a) {
   if (!schedule(a, blockIdx.x, bh, qb)) return;
   const int64_t rowid = (int64_t)bh * a.nqb + qb;
   // (read-first-lane: row values are wave-uniform and should live in scalar registers)
-  const int cnt = __builtin_amdgcn_readfirstlane(min(max(a.cnt[rowid], 0), a.nkb));   // never past nkb slots
+  const int cnt_row = __builtin_amdgcn_readfirstlane(min(max(a.cnt[rowid], 0), a.nkb));   // never past nkb slots
+  // a split frame-0 row: this item walks entries lo .. lo + cnt - 1 of the list
+  const bool part_item = a.split > 1 && (int)blockIdx.x < a.n_dense;
+  const int part = part_item ? (int)blockIdx.x % a.split : 0;
+  const int lo = part_item ? (int)((int64_t)part * cnt_row / a.split) : 0;
+  const int cnt = part_item ? (int)((int64_t)(part + 1) * cnt_row / a.split) - lo : cnt_row;
   const int nsub = (cnt * BK + SUB - 1) / SUB;          // 32-key sub-tiles of the row
 
   const T* Qb = reinterpret_cast<const T*>(a.q) + (int64_t)bh * a.seq_alloc * D;
@@ -286,10 +292,11 @@ void fwd_kernel(FwdArgs a) {
   // loads, lane b taking part b, several steps before they are needed: the
   // loads are ordered with the tile loads, so no wait on them ever blocks the
   // LDS reads (as a scalar-cache load's wait would).
-  const uint32_t lbytes = (uint32_t)a.nkb * 4u;
-  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + rowid * a.nkb), 0, (int)lbytes, 0x00020000);
+  const uint32_t lbytes = (uint32_t)(a.nkb - lo) * 4u;
+  const int64_t lbase = rowid * a.nkb + lo;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + lbase), 0, (int)lbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(has_w ? (void*)(a.logw + rowid * a.nkb) : (void*)(a.idx + rowid * a.nkb), 0,
+      __builtin_amdgcn_make_buffer_rsrc(has_w ? (void*)(a.logw + lbase) : (void*)(a.idx + lbase), 0,
                                         (int)lbytes, 0x00020000);
   struct Raw {
     int j;      // lane b: list entry of part b
@@ -912,15 +919,26 @@ void fwd_kernel(FwdArgs a) {
   // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
   // 16 rows of float32 per pass in K slot 0, 16-byte chunks XOR-swizzled by
   // the row so the column writes of 16 rows fall on distinct banks.
+  // A part of a split row leaves O unnormalized, with its reference max and
+  // row sum, in its workspace slot instead.
   float* ostage = reinterpret_cast<float*>(k_lds0);
   T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
+  constexpr int QB = 32 * QT;
+  float* wsO = part_item ? a.ws + (int64_t)blockIdx.x * QB * D : nullptr;
+  float* wsM = part_item ? a.ws + (int64_t)a.n_dense * QB * D + (int64_t)blockIdx.x * QB : nullptr;
+  float* wsL = part_item ? wsM + (int64_t)a.n_dense * QB : nullptr;
   constexpr int C8 = D / 8;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l = add_xor32(l_run[qt]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = part_item ? 1.0f : (l > 0.0f ? 1.0f / l : 0.0f);
     const int64_t qrow0 = q0 + 32 * qt;
-    if (hf == 0 && a.lse) {
+    if (part_item) {
+      if (hf == 0) {
+        wsM[32 * qt + qc] = m_run[qt];
+        wsL[32 * qt + qc] = l;
+      }
+    } else if (hf == 0 && a.lse) {
       const int64_t row = qrow0 + qc;
       const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
       if (row < a.seq_alloc)
@@ -957,10 +975,68 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int c = 0; c < 8; ++c) v[c] = 0.0f;
         }
-        store8<T>(Ob + row * D + c8 * 8, v);
+        if (part_item) store8<float>(wsO + (row - q0) * D + c8 * 8, v);
+        else store8<T>(Ob + row * D + c8 * 8, v);
       }
     }
   }
+}
+
+// Merge of the parts of split frame-0 rows.  Part p of a row holds, per
+// query row, unnormalized O_p, the reference max m_p (log2 domain) and the
+// row sum l_p of its own key blocks; with M = max_p m_p and w_p = 2^(m_p - M)
+// the row's attention over the union of the parts is sum_p w_p O_p divided
+// by sum_p w_p l_p, and its LSE is (M + log2 sum_p w_p l_p) ln 2: the same
+// exact softmax the one-wave row computes (AB-Attention page, TL;DR).  A part
+// with no keys (m_p = -inf) adds nothing; a row with none is 0, LSE -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(FwdArgs a) {
+  constexpr int C8 = D / 8;
+  const int r = blockIdx.x;                        // split row: items r * split .. + split - 1
+  const int bh = r % a.BH, qb = a.dense_first + r / a.BH;
+  const int QB = a.q_block, P = a.split;
+  const int64_t q0 = (int64_t)qb * QB;
+  const float* wsO = a.ws;
+  const float* wsM = a.ws + (int64_t)a.n_dense * QB * D;
+  const float* wsL = wsM + (int64_t)a.n_dense * QB;
+  T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
+  for (int e = threadIdx.x; e < QB * C8; e += 256) {
+    const int q = e / C8, c8 = e % C8;
+    const int64_t row = q0 + q;
+    if (row >= a.seq_alloc) continue;
+    float M = -INFINITY;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, wsM[((int64_t)r * P + p) * QB + q]);
+    float L = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      const int64_t it = (int64_t)r * P + p;
+      const float mp = wsM[it * QB + q];
+      if (mp == -INFINITY) continue;
+      const float w = exp2f(mp - M);
+      L += w * wsL[it * QB + q];
+      const float4* src = reinterpret_cast<const float4*>(wsO + (it * QB + q) * D + c8 * 8);
+      const float4 x = src[0], y = src[1];
+      acc[0] += w * x.x; acc[1] += w * x.y; acc[2] += w * x.z; acc[3] += w * x.w;
+      acc[4] += w * y.x; acc[5] += w * y.y; acc[6] += w * y.z; acc[7] += w * y.w;
+    }
+    const bool live = row < a.S && L > 0.0f;
+    const float inv = live ? 1.0f / L : 0.0f;
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = live ? acc[c] * inv : 0.0f;
+    store8<T>(Ob + row * D + c8 * 8, v);
+    if (c8 == 0 && a.lse) a.lse[(int64_t)bh * a.seq_alloc + row] = live ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T>
+hipError_t launch_merge(const FwdArgs& a, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.n_dense / a.split)), block(256);
+  if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<T, 64>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((merge_kernel<T, 128>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 template <typename T, int D, int QT>
@@ -989,7 +1065,9 @@ hipError_t launch_d(const FwdArgs& a, int head_dim, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream) {
-  return dtype == 0 ? launch_d<bf16_t>(a, head_dim, stream) : launch_d<float>(a, head_dim, stream);
+  const hipError_t e = dtype == 0 ? launch_d<bf16_t>(a, head_dim, stream) : launch_d<float>(a, head_dim, stream);
+  if (e != hipSuccess || a.split <= 1 || a.n_dense == 0) return e;
+  return dtype == 0 ? launch_merge<bf16_t>(a, head_dim, stream) : launch_merge<float>(a, head_dim, stream);
 }
 
 }  // namespace bsa

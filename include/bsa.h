@@ -233,6 +233,39 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, int32_t d
                           const float* log_w, float softmax_scale, void* out, float* lse,
                           const bsa_forward_options* opt, void* stream);
 
+/* bsa_forward_ex with the key lists of the frame-0 query blocks split over
+ * `dense_split` work items each (the rows the frame-0 override makes dense:
+ * "Attention matrix view: make only frame-0 query rows dense", sec. 2 and 4).
+ * Part p of such a row walks list entries floor(p*cnt/P) .. floor((p+1)*cnt/P)-1
+ * and leaves its partial softmax state in `workspace`; a second kernel on the
+ * same stream merges the parts into out and lse (the same exact softmax over
+ * the union of the blocks, up to rounding: not bit-identical to the one-wave
+ * row).  Worth it when there are few rows per SIMD, so that a frame-0 row
+ * walking all nkb blocks alone would outlast the rest of the launch; the
+ * other rows are unchanged.
+ *   dense_split: 1..16 (1: exactly bsa_forward_ex; ignored if the geometry
+ *                has no frame-0 rows).
+ *   workspace:   caller-owned device memory of at least
+ *                bsa_forward_split_workspace_bytes(g, dense_split) bytes,
+ *                16-byte aligned (may be NULL when that size is 0); its
+ *                contents on entry do not matter, and it holds partial
+ *                states until the merge has run.  Calls that overlap on one
+ *                workspace race.
+ *   Errors: as bsa_forward_ex; also dense_split outside 1..16, or a NULL,
+ *   misaligned or short workspace when one is needed
+ *   (BSA_ERR_INVALID_ARGUMENT, before any launch). */
+bsa_status bsa_forward_split(const void* q, const void* k, const void* v, int32_t dtype,
+                             const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                             const float* log_w, float softmax_scale, void* out, float* lse,
+                             const bsa_forward_options* opt, int32_t dense_split, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes bsa_forward_split needs: B*H*(frame-0 query blocks)*
+ * dense_split*(q_block*D + 2*q_block)*4, or 0 when dense_split is 1 or there
+ * are no frame-0 rows.  Errors: NULL bytes, dense_split outside 1..16
+ * (BSA_ERR_INVALID_ARGUMENT), or any geometry error. */
+bsa_status bsa_forward_split_workspace_bytes(const bsa_geometry* g, int32_t dense_split, int64_t* bytes);
+
 /* Intra-block clustering selector, step 1: block importance (AB-Attention
  * page, TL;DR item 1 and the flowchart's intra-block cluster node: queries
  * are clustered only inside their own query block; EG-Sparse page Eq. 2 for

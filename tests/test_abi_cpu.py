@@ -87,6 +87,23 @@ def test_validation_rejects_before_launch():
     assert L.bsa_forward(fake, fake, fake, 0, ctypes.byref(small), fake, fake, None, 0.0, fake, None,
                          None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert b"seq_alloc" in L.bsa_last_error()
+    # the key split: its range, and its workspace when frame-0 rows exist
+    opt = _lib.bsa_forward_options(0)
+    fwd_split = lambda split, ws, nbytes: L.bsa_forward_split(  # noqa: E731
+        fake, fake, fake, 0, ctypes.byref(g), fake, fake, None, 0.0, fake, None, ctypes.byref(opt), split, ws,
+        nbytes, None)
+    need = ctypes.c_int64(0)
+    assert L.bsa_forward_split_workspace_bytes(ctypes.byref(g), 2, ctypes.byref(need)) == _lib.BSA_OK
+    assert need.value == 12 * 25 * 2 * (64 * 128 + 2 * 64) * 4      # small_bf16: 25 frame-0 query blocks
+    for split in (0, 17):
+        assert fwd_split(split, fake, need.value) == _lib.BSA_ERR_INVALID_ARGUMENT
+        assert L.bsa_forward_split_workspace_bytes(ctypes.byref(g), split, ctypes.byref(need)) == \
+            _lib.BSA_ERR_INVALID_ARGUMENT
+    L.bsa_forward_split_workspace_bytes(ctypes.byref(g), 2, ctypes.byref(need))
+    assert fwd_split(2, None, need.value) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert fwd_split(2, mis, need.value) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert fwd_split(2, fake, need.value - 1) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert b"workspace" in L.bsa_last_error()
     # 4096 heads x 2^20 query blocks: more block rows than one launch counts
     huge = _lib.bsa_geometry(1, 4096, 1 << 26, 0, 0, 0, 128, 64, 64, 0, 1 << 26)
     assert L.bsa_pool_blocks(fake, 0, ctypes.byref(huge), 64, fake, None) == _lib.BSA_ERR_UNSUPPORTED

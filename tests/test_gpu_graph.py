@@ -5,7 +5,8 @@ caller can capture pooling, a block selector and the forward on one stream
 and replay them.  Each case here runs the path eagerly, captures it once,
 then replays the graph three times: the outputs are overwritten with junk by
 eager kernels before every replay, and new inputs are copied into the
-captured input buffers before the third.  Every replay must reproduce, bit
+captured input buffers before the third.  The key split of the frame-0 rows
+(a forward plus a merge kernel, with its workspace) is captured the same way.  Every replay must reproduce, bit
 for bit, the eager path on the same inputs (counts, the listed prefix of
 every row, masks, log-weights, output and LSE).
 """
@@ -50,6 +51,11 @@ def _path(case, g, q, k, v, head_class):
         kp = bsa.bsa_pool_blocks(k, g, g.k_block)
         mask, cnt, idx, logw = bsa.bsa_build_mask(qp, kp, g, bsa.MaskParams(keep_ratio=0.3, frame0_dense=True))
         out, lse = bsa.bsa_forward(q, k, v, g, cnt, idx, logw, want_lse=True)
+    elif case == "split":
+        qp = bsa.bsa_pool_blocks(q, g, g.q_block)
+        kp = bsa.bsa_pool_blocks(k, g, g.k_block)
+        mask, cnt, idx, logw = bsa.bsa_build_mask(qp, kp, g, bsa.MaskParams(keep_ratio=0.3, frame0_dense=True))
+        out, lse = bsa.bsa_forward(q, k, v, g, cnt, idx, logw, want_lse=True, dense_split=3)
     elif case == "sample":
         qp = bsa.bsa_pool_blocks(q, g, g.q_block)
         kp = bsa.bsa_pool_blocks(k, g, g.k_block)
@@ -110,7 +116,7 @@ def _junk(res):
             t.fill_(-7)
 
 
-@pytest.mark.parametrize("case,bk", [("topk", 64), ("sample", 16), ("cluster", 64), ("top_p", 64),
+@pytest.mark.parametrize("case,bk", [("topk", 64), ("split", 64), ("sample", 16), ("cluster", 64), ("top_p", 64),
                                      ("structured", 64)])
 def test_path_replays_from_one_graph(case, bk):
     w = _workload(bk)
