@@ -241,3 +241,35 @@ def test_header_is_c99_and_a_c_client_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([out], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_dense_split_suggestion():
+    """The key split suggested for the frame-0 rows: their length over the
+    launch's average blocks per SIMD, rounded, within 1..8, >= 16 blocks a part
+    (host logic only: the SIMD count is given, the counts are a CPU tensor)."""
+    import torch
+
+    def counts(w, dense_len, other_len):
+        g = _geo(w)
+        d = bsa.bsa_derive(g)
+        c = torch.full((w.B, w.H, d["nqb"]), other_len, dtype=torch.int32)
+        c[:, :, d["frame0_first"]:d["frame0_last"] + 1] = dense_len
+        return g, c
+
+    small = W.workload("small_bf16")                  # 12 heads x 122 query blocks, 25 of them frame 0
+    g, c = counts(small, 122, 31)
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 2        # 122 blocks against 71 per SIMD
+    head = W.workload("wan_1p3b_keep10")              # 512-block frame-0 rows, 447 per SIMD
+    g, c = counts(head, 512, 52)
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 1
+    g, c = counts(head, 512, 4)                       # 512 against 173 per SIMD
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 3
+    g, c = counts(head.replace(H=1), 512, 0)          # one head: 512 against 12.5, capped at 8
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 8
+    g, c = counts(small.replace(H=1), 122, 0)         # 122 against 3: at least 16 blocks a part
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 7
+    tiny = W.workload("tiny_f32")                     # 7-block rows: shorter than two 16-block parts
+    g, c = counts(tiny, 7, 2)
+    assert bsa.suggest_dense_split(g, c, simds=1024) == 1
+    g = bsa.Geometry(1, 2, 64, 0, 0, 0, 64, 32, 32, 64)    # text only: no frame-0 rows
+    assert bsa.suggest_dense_split(g, torch.full((1, 2, 2), 2, dtype=torch.int32), simds=1024) == 1
