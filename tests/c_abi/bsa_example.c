@@ -8,7 +8,10 @@
  * runs bsa_pool_blocks on Q and K, bsa_build_mask (top-k with frame-0 rows
  * dense) and bsa_forward (with the LSE), and writes DIR/cnt.bin (int32
  * [B, H, nqb]), DIR/idx.bin (int32 [B, H, nqb, nkb]), DIR/out.bin (bf16 bits)
- * and DIR/lse.bin (float32 [B, H, SEQ_ALLOC]).  Exit status 0 on success.
+ * and DIR/lse.bin (float32 [B, H, SEQ_ALLOC]); then bsa_forward_split with
+ * the frame-0 rows split in two (its workspace from
+ * bsa_forward_split_workspace_bytes) into DIR/out_split.bin and
+ * DIR/lse_split.bin.  Exit status 0 on success.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -143,6 +146,23 @@ int main(int argc, char** argv) {
     fprintf(stderr, "cannot write results to %s\n", dir);
     return 7;
   }
+
+  /* the same forward with the frame-0 rows' key lists split in two */
+  int64_t ws_bytes = 0;
+  BSA_OK_(bsa_forward_split_workspace_bytes(&g, 2, &ws_bytes));
+  void* ws = NULL;
+  if (ws_bytes > 0) HIP_OK(hipMalloc(&ws, (size_t)ws_bytes));
+  BSA_OK_(bsa_forward_split(q, k, v, BSA_DTYPE_BF16, &g, cnt, idx, NULL, 0.0f, out, lse, NULL, 2, ws, ws_bytes,
+                            NULL));
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(ho, out, n_x * 2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(hlse, lse, BH * (size_t)g.seq_alloc * 4, hipMemcpyDeviceToHost));
+  if (write_file(dir, "out_split.bin", ho, n_x * 2) ||
+      write_file(dir, "lse_split.bin", hlse, BH * (size_t)g.seq_alloc * 4)) {
+    fprintf(stderr, "cannot write results to %s\n", dir);
+    return 7;
+  }
+  if (ws) hipFree(ws);
 
   /* an invalid call is rejected on the host with a message */
   bsa_geometry bad = g;

@@ -1,7 +1,8 @@
 """The C ABI from a plain C client on the GPU.
 
 tests/c_abi/bsa_example (built by build()) runs pooling, the top-k mask and
-the forward through include/bsa.h with only the HIP runtime's C API.  Its
+the forward (plain, and with the frame-0 rows' key lists split in two)
+through include/bsa.h with only the HIP runtime's C API.  Its
 counts, lists, output and LSE must equal, bit for bit, what the Python
 binding gets from the same library on the same inputs; the lists are also
 checked against the oracle.
@@ -70,6 +71,14 @@ def test_c_client_matches_the_binding(tmp_path):
                 assert np.array_equal(idx[b, h, i, :n], i2[b, h, i, :n]), (b, h, i)
     assert np.array_equal(out, o2.view(torch.int16).cpu().numpy())
     assert np.array_equal(lse, l2.cpu().numpy())
+    # the key-split forward: the binding's, bit for bit
+    outs = np.fromfile(str(tmp_path / "out_split.bin"), dtype=np.int16).reshape(w.B, w.H, w.seq_alloc, w.D)
+    lses = np.fromfile(str(tmp_path / "lse_split.bin"), dtype=np.float32).reshape(w.B, w.H, w.seq_alloc)
+    o3, l3 = bsa.bsa_forward(qc, kc, vc, gg, torch.from_numpy(c2).cuda(), torch.from_numpy(i2).cuda(), None,
+                             want_lse=True, dense_split=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(outs, o3.view(torch.int16).cpu().numpy())
+    assert np.array_equal(lses.view(np.uint32), l3.cpu().numpy().view(np.uint32))
     # and the lists are the oracle's
     _, ocnt, oidx, _ = oracle.build_mask(oracle.pool_blocks(q, g.S, g.q_block),
                                          oracle.pool_blocks(k, g.S, g.k_block), g, params_of(w))
