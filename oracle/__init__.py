@@ -8,7 +8,8 @@ leg of ``bench.py``; the library never imports, links or runs it.  See
 ``oracle/structured.py`` for the structured (per-head frame context) lists.
 """
 from .reference import *  # noqa: F401,F403
-from .reference import (Geometry, MaskParams, attention, attention_head, block_logits,  # noqa: F401
+from .reference import (Geometry, MaskParams, attention, attention_head, attention_head_gathered,  # noqa: F401
+                        block_logits,
                         build_mask, exp_spec, fold_sum, inclusion_probabilities,
                         philox4x64_10, pool_blocks, sample_uniforms, select_sample,
                         select_topk, topk_count, score_scale, forward_scale,

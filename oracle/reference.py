@@ -481,6 +481,47 @@ def attention_head(q, k, v, g: Geometry, cnt_h, idx_h, logw_h,
     return np.concatenate(outs, axis=0), np.concatenate(lses)
 
 
+def attention_head_gathered(q, k, v, g: Geometry, cnt_h, idx_h, logw_h,
+                            q_blocks=None, softmax_scale: float = 0.0):
+    """attention_head with the key tokens of each row's listed blocks gathered
+    first, so its cost follows the selected blocks rather than the whole
+    sequence (AB-Attention page, TL;DR: attention is computed only on the
+    selected blocks).  The excluded keys of attention_head contribute exp(-inf)
+    = 0 there, so both give the same float64 softmax up to summation order.
+    Used as a CPU speed reference; the parity oracle is attention_head."""
+    S, bq, bk = g.S, g.q_block, g.k_block
+    scale = forward_scale(g.head_dim, softmax_scale)
+    if q_blocks is None:
+        q_blocks = range(g.nqb)
+    K = np.asarray(k[:S], dtype=np.float64)
+    V = np.asarray(v[:S], dtype=np.float64)
+    outs, lses = [], []
+    for i in q_blocks:
+        lo, hi = i * bq, min((i + 1) * bq, g.seq_alloc)
+        O = np.zeros((hi - lo, g.head_dim))
+        L = np.full(hi - lo, -np.inf)
+        c = int(cnt_h[i])
+        if c > 0:
+            blocks = np.asarray(idx_h[i, :c])
+            toks = (blocks[:, None] * bk + np.arange(bk)[None, :]).ravel()
+            bias = np.repeat(np.asarray(logw_h[i, :c], dtype=np.float64), bk)
+            keep = toks < S
+            toks, bias = toks[keep], bias[keep]
+            Q = np.asarray(q[lo:hi], dtype=np.float64)
+            logits = (Q @ K[toks].T) * scale + bias[None, :]
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            s = e.sum(axis=1, keepdims=True)
+            O = (e / s) @ V[toks]
+            L = (m + np.log(s))[:, 0]
+            valid = np.arange(lo, hi) < S
+            O[~valid] = 0.0
+            L[~valid] = -np.inf
+        outs.append(O)
+        lses.append(L)
+    return np.concatenate(outs, axis=0), np.concatenate(lses)
+
+
 def attention(q, k, v, g: Geometry, cnt, idx, logw, softmax_scale: float = 0.0):
     """attention_head over every (b, h): O [B,H,seq_alloc,D], LSE [B,H,seq_alloc]."""
     O = np.zeros((g.B, g.H, g.seq_alloc, g.head_dim))

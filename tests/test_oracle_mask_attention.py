@@ -234,3 +234,24 @@ def test_horvitz_thompson_parts_are_unbiased():
     sd = np.sqrt(np.maximum(den2 / n - mean ** 2, 0) / n)
     assert np.all(np.abs(mean - den_d) <= 5 * sd + 1e-9 * den_d)
     assert np.allclose(num / n, num_d, atol=6 * np.abs(num_d).max() * sd.max() / mean.min() + 0.05 * np.abs(num_d).max())
+
+
+def test_block_gathered_attention_equals_token_expanded():
+    """The block-gathered CPU speed reference is the oracle's softmax: random
+    lists (ragged last block), random log-weights, an empty row, pad rows."""
+    w = tiny(text_len=5, frames=3, lh=3, lw=7, bq=8, bk=8, D=16, H=2, topk=3)
+    g, (q, k, v), _, p, (mask, cnt, idx, logw) = _mask_for(w)
+    rng = np.random.default_rng(3)
+    lw = logw.copy()
+    lw[cnt[..., None] > np.arange(g.nkb)] = rng.standard_normal((cnt.sum(),)).astype(np.float32)
+    cnt2 = cnt.copy()
+    cnt2[0, 1, 2] = 0
+    for b in range(g.B):
+        for h in range(g.H):
+            O, L = oracle.attention_head(q[b, h], k[b, h], v[b, h], g, cnt2[b, h], idx[b, h], lw[b, h])
+            Og, Lg = oracle.attention_head_gathered(q[b, h], k[b, h], v[b, h], g, cnt2[b, h], idx[b, h], lw[b, h])
+            assert np.allclose(Og, O, rtol=0, atol=1e-12) and np.array_equal(np.isneginf(Lg), np.isneginf(L))
+            fin = np.isfinite(L)
+            assert np.allclose(Lg[fin], L[fin], rtol=0, atol=1e-12)
+    # the last key block is ragged (S is not a multiple of 8) and is in some list
+    assert g.S % g.k_block != 0 and (idx[cnt[..., None] > np.arange(g.nkb)] == g.nkb - 1).any()
