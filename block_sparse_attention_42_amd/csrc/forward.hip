@@ -992,18 +992,21 @@ void fwd_kernel(FwdArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(FwdArgs a) {
   constexpr int C8 = D / 8;
-  const int r = blockIdx.x;                        // split row: items r * split .. + split - 1
-  const int bh = r % a.BH, qb = a.dense_first + r / a.BH;
   const int QB = a.q_block, P = a.split;
+  const int per_row = (QB * C8 + 255) / 256;       // workgroups per split row
+  const int r = blockIdx.x / per_row;              // split row: items r * split .. + split - 1
+  const int bh = r % a.BH, qb = a.dense_first + r / a.BH;
   const int64_t q0 = (int64_t)qb * QB;
   const float* wsO = a.ws;
   const float* wsM = a.ws + (int64_t)a.n_dense * QB * D;
   const float* wsL = wsM + (int64_t)a.n_dense * QB;
   T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
-  for (int e = threadIdx.x; e < QB * C8; e += 256) {
+  {
+    const int e = (blockIdx.x % per_row) * 256 + threadIdx.x;   // (query row, 8-channel chunk) of the row
+    if (e >= QB * C8) return;
     const int q = e / C8, c8 = e % C8;
     const int64_t row = q0 + q;
-    if (row >= a.seq_alloc) continue;
+    if (row >= a.seq_alloc) return;
     float M = -INFINITY;
     for (int p = 0; p < P; ++p) M = fmaxf(M, wsM[((int64_t)r * P + p) * QB + q]);
     float L = 0.0f;
@@ -1033,7 +1036,8 @@ __global__ __launch_bounds__(256) void merge_kernel(FwdArgs a) {
 
 template <typename T>
 hipError_t launch_merge(const FwdArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.n_dense / a.split)), block(256);
+  const int per_row = (a.q_block * (head_dim / 8) + 255) / 256;
+  const dim3 grid((unsigned)((int64_t)(a.n_dense / a.split) * per_row)), block(256);
   if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<T, 64>), grid, block, 0, stream, a);
   else hipLaunchKernelGGL((merge_kernel<T, 128>), grid, block, 0, stream, a);
   return hipGetLastError();
