@@ -446,6 +446,8 @@ def main():
         "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "pool_ms": round(pool_ms, 4),
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+        "pool_hbm": {"bound": "hbm", "achieved": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "mask_ms": round(mask_ms, 4),
         "mask_gbs": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
         "mask_valu": {"bound": "alu", "achieved": round(mask_lane_ops / (mask_ms * 1e-3) / 1e12, 2),
