@@ -289,7 +289,8 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
                 kv_cnt: torch.Tensor, kv_idx: torch.Tensor, log_w: Optional[torch.Tensor] = None,
                 softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = False, launch_order: str = "frame_position",
-                stream=None, _ex: bool = False, dense_split: int = 1, workspace: Optional[torch.Tensor] = None):
+                stream=None, _ex: bool = False, dense_split: int = 1, workspace: Optional[torch.Tensor] = None,
+                static_workspace: bool = False):
     """Attention of every query block over its listed key blocks.  Returns (out, lse or None).
 
     ``launch_order`` ("frame_position" or "frame_runs", see LAUNCH_ORDERS) only
@@ -297,7 +298,10 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
     ``dense_split`` > 1 splits each frame-0 row's list over that many work
     items and merges their partial states (bsa_forward_split, with
     ``workspace`` or a new one of bsa_forward_split_workspace_bytes bytes);
-    see suggest_dense_split."""
+    see suggest_dense_split.  ``static_workspace`` runs the split through
+    bsa_forward_split_static instead: its partial states go to the library's
+    own device scratch (BSA_SPLIT_STATIC_MAX_BYTES per GPU), so the call
+    allocates nothing beyond ``out`` and ``lse`` when they are not given."""
     if launch_order not in LAUNCH_ORDERS:
         raise ValueError(f"launch_order {launch_order!r} not in {sorted(LAUNCH_ORDERS)}")
     d = bsa_derive(g)
@@ -320,7 +324,12 @@ def bsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geometry,
         _need(lse, "lse", (g.B, g.H, g.seq_alloc), torch.float32, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(g.c()), _ptr(kv_cnt), _ptr(kv_idx),
             _ptr(log_w), ctypes.c_float(softmax_scale), _ptr(out), _ptr(lse))
-    if dense_split != 1:
+    if static_workspace:
+        if workspace is not None:
+            raise ValueError("static_workspace and workspace exclude each other")
+        opt = _lib.bsa_forward_options(LAUNCH_ORDERS[launch_order])
+        _lib.check(_lib.lib().bsa_forward_split_static(*args, ctypes.byref(opt), int(dense_split), _stream(stream)))
+    elif dense_split != 1:
         nbytes = bsa_forward_split_workspace_bytes(g, dense_split)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)

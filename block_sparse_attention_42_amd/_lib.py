@@ -13,9 +13,10 @@ BSA_DTYPE_BF16 = 0
 BSA_DTYPE_F32 = 1
 BSA_SELECT_TOPK = 0
 BSA_SELECT_SAMPLE = 1
+BSA_SPLIT_STATIC_MAX_BYTES = 33554432
 
 EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
-            "bsa_forward_split", "bsa_forward_split_workspace_bytes",
+            "bsa_forward_split", "bsa_forward_split_workspace_bytes", "bsa_forward_split_static",
             "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes", "bsa_select_top_p",
             "bsa_frame_scores", "bsa_classify_heads", "bsa_structured_lists",
             "bsa_status_string", "bsa_last_error", "bsa_abi_version"]
@@ -83,6 +84,8 @@ def lib():
                                      ctypes.POINTER(bsa_forward_options), P]
         L.bsa_forward_split.argtypes = [P, P, P, ctypes.c_int32, G, P, P, P, ctypes.c_float, P, P,
                                         ctypes.POINTER(bsa_forward_options), ctypes.c_int32, P, ctypes.c_int64, P]
+        L.bsa_forward_split_static.argtypes = [P, P, P, ctypes.c_int32, G, P, P, P, ctypes.c_float, P, P,
+                                               ctypes.POINTER(bsa_forward_options), ctypes.c_int32, P]
         L.bsa_forward_split_workspace_bytes.argtypes = [G, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
         L.bsa_cluster_importance.argtypes = [P, ctypes.c_int32, P, G, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.c_int32, P, P]
@@ -94,7 +97,8 @@ def lib():
         L.bsa_classify_heads.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
         L.bsa_structured_lists.argtypes = [P, G, ctypes.POINTER(bsa_struct_params), P, P, P, P]
         for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
-                  "bsa_forward_split", "bsa_forward_split_workspace_bytes", "bsa_abi_version",
+                  "bsa_forward_split", "bsa_forward_split_workspace_bytes", "bsa_forward_split_static",
+                  "bsa_abi_version",
                   "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes",
                   "bsa_select_top_p", "bsa_frame_scores", "bsa_classify_heads", "bsa_structured_lists"):
             getattr(L, f).restype = ctypes.c_int32

@@ -483,7 +483,7 @@ int32_t dense_rows(const Derived& d) { return d.f0_first >= 0 ? d.f0_last - d.f0
 bsa_status forward_impl(const void* q, const void* k, const void* v, int32_t dtype, const bsa_geometry* g,
                         const int32_t* kv_cnt, const int32_t* kv_idx, const float* log_w, float softmax_scale,
                         void* out, float* lse, const bsa_forward_options* opt, int32_t split, void* workspace,
-                        int64_t workspace_bytes, void* stream) {
+                        int64_t workspace_bytes, void* stream, bool static_ws = false) {
   const int32_t order = opt ? opt->launch_order : BSA_ORDER_FRAME_POSITION;
   if (order != BSA_ORDER_FRAME_POSITION && order != BSA_ORDER_FRAME_RUNS)
     return fail(BSA_ERR_INVALID_ARGUMENT, "unknown launch order %d", order);
@@ -529,6 +529,20 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, int32_t dty
   const int32_t nd = dense_rows(d);
   if (split < 1 || split > 16) return fail(BSA_ERR_INVALID_ARGUMENT, "dense_split %d must be in 1..16", split);
   if (nd == 0) split = 1;                        // no frame-0 rows: nothing to split
+  if (split > 1 && static_ws) {
+    // the library's own scratch: checked against its size, looked up last
+    const int64_t need = bsa::split_ws_floats((int64_t)a.BH * nd * split, g->q_block, g->head_dim) * 4;
+    if (need > bsa::kStaticScratchBytes)
+      return fail(BSA_ERR_UNSUPPORTED, "the key split needs %lld bytes of scratch, more than the %lld the library "
+                  "holds", (long long)need, (long long)bsa::kStaticScratchBytes);
+    if ((int64_t)a.BH * nd * split > 0x7fffffffLL)
+      return fail(BSA_ERR_UNSUPPORTED, "too many query blocks for one launch");
+    float* ws = nullptr;
+    const hipError_t e = bsa::static_scratch(&ws);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "device scratch lookup: %s", hipGetErrorString(e));
+    workspace = ws;
+    workspace_bytes = bsa::kStaticScratchBytes;
+  }
   if (split > 1) {
     const int64_t need = bsa::split_ws_floats((int64_t)a.BH * nd * split, g->q_block, g->head_dim) * 4;
     if (!workspace || !aligned16(workspace))
@@ -586,6 +600,16 @@ bsa_status bsa_forward_split(const void* q, const void* k, const void* v, int32_
                              int64_t workspace_bytes, void* stream) {
   return forward_impl(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, opt, dense_split,
                       workspace, workspace_bytes, stream);
+}
+
+static_assert(BSA_SPLIT_STATIC_MAX_BYTES == bsa::kStaticScratchBytes, "header and library scratch sizes differ");
+
+bsa_status bsa_forward_split_static(const void* q, const void* k, const void* v, int32_t dtype,
+                                    const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                                    const float* log_w, float softmax_scale, void* out, float* lse,
+                                    const bsa_forward_options* opt, int32_t dense_split, void* stream) {
+  return forward_impl(q, k, v, dtype, g, kv_cnt, kv_idx, log_w, softmax_scale, out, lse, opt, dense_split, nullptr,
+                      0, stream, true);
 }
 
 }  // extern "C"

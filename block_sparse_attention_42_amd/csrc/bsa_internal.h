@@ -146,6 +146,12 @@ inline int64_t split_ws_floats(int64_t items, int32_t q_block, int32_t D) {
 constexpr int kXcds = 8;
 inline int64_t forward_grid(const FwdArgs& a) { return (int64_t)a.n_dense + (int64_t)kXcds * a.per_xcd; }
 
+// Device scratch owned by the library (scratch.hip): the partial states of
+// bsa_forward_split_static, at most this many bytes on each GPU.
+constexpr int64_t kStaticScratchBytes = 32LL << 20;
+// Device address of the current GPU's copy (looked up once per device).
+hipError_t static_scratch(float** ptr);
+
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 int importance_group(int C, int nkb, int nqb);

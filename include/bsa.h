@@ -266,6 +266,29 @@ bsa_status bsa_forward_split(const void* q, const void* k, const void* v, int32_
  * (BSA_ERR_INVALID_ARGUMENT), or any geometry error. */
 bsa_status bsa_forward_split_workspace_bytes(const bsa_geometry* g, int32_t dense_split, int64_t* bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * bsa_forward_split with its workspace in scratch memory the library owns,
+ * a static device array of BSA_SPLIT_STATIC_MAX_BYTES that each GPU holds
+ * from the library's first use of it on that device until the process ends.
+ * The call allocates nothing; the caller still owns every input and output.
+ * The first call on a device looks the array's device address up (one HIP
+ * runtime call, made outside a capture on that device); later calls make no
+ * runtime call besides their launches.  Every call on a GPU shares that
+ * GPU's array: calls whose launches overlap on one GPU (on different
+ * streams, or from different threads) race, and must be ordered by the
+ * caller.  Nothing in the array needs clearing: each call writes every
+ * partial state it merges.
+ *   Errors: as bsa_forward_split; a split that needs more than
+ *   BSA_SPLIT_STATIC_MAX_BYTES (bsa_forward_split_workspace_bytes) gives
+ *   BSA_ERR_UNSUPPORTED before any launch; a failed address lookup gives
+ *   BSA_ERR_HIP. */
+#define BSA_SPLIT_STATIC_MAX_BYTES 33554432
+bsa_status bsa_forward_split_static(const void* q, const void* k, const void* v, int32_t dtype,
+                                    const bsa_geometry* g, const int32_t* kv_cnt, const int32_t* kv_idx,
+                                    const float* log_w, float softmax_scale, void* out, float* lse,
+                                    const bsa_forward_options* opt, int32_t dense_split, void* stream);
+
 /* Intra-block clustering selector, step 1: block importance (AB-Attention
  * page, TL;DR item 1 and the flowchart's intra-block cluster node: queries
  * are clustered only inside their own query block; EG-Sparse page Eq. 2 for

@@ -104,6 +104,17 @@ def test_validation_rejects_before_launch():
     assert fwd_split(2, mis, need.value) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert fwd_split(2, fake, need.value - 1) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert b"workspace" in L.bsa_last_error()
+    # the allocation-free split: validated like the split, then held to the library's scratch size
+    fwd_static = lambda split, geo=g, qp=fake: L.bsa_forward_split_static(  # noqa: E731
+        qp, fake, fake, 0, ctypes.byref(geo), fake, fake, None, 0.0, fake, None, ctypes.byref(opt), split, None)
+    for split in (0, 17):
+        assert fwd_static(split) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert fwd_static(2, qp=None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    hy = _geo(W.workload("hunyuan_keep08")).c()
+    L.bsa_forward_split_workspace_bytes(ctypes.byref(hy), 16, ctypes.byref(need))
+    assert need.value > _lib.BSA_SPLIT_STATIC_MAX_BYTES
+    assert fwd_static(16, geo=hy) == _lib.BSA_ERR_UNSUPPORTED
+    assert b"scratch" in L.bsa_last_error()
     # 4096 heads x 2^20 query blocks: more block rows than one launch counts
     huge = _lib.bsa_geometry(1, 4096, 1 << 26, 0, 0, 0, 128, 64, 64, 0, 1 << 26)
     assert L.bsa_pool_blocks(fake, 0, ctypes.byref(huge), 64, fake, None) == _lib.BSA_ERR_UNSUPPORTED
