@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libbsa.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "topp.hip", "structured.hip", "forward.hip", "scratch.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "mask.hip", "cluster.hip", "topp.hip", "structured.hip", "forward.hip", "forward_wide.hip", "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are switched off for every device pass.
@@ -25,6 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # The forward's hand-ordered pipeline schedules best with the ILP-maximizing
 # machine scheduler (measured on MI355X: 1-2.5 % faster than the default).
 EXTRA = {"forward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+         "forward_wide.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
          "pool.hip": ["-ffp-contract=off"], "mask.hip": ["-ffp-contract=off"],
          "cluster.hip": ["-ffp-contract=off"], "topp.hip": ["-ffp-contract=off"],
          "abi.cpp": ["-x", "hip", "-ffp-contract=off"]}

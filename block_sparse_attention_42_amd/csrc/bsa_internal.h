@@ -162,5 +162,9 @@ hipError_t launch_frame_scores(const StructArgs& a, hipStream_t stream);
 hipError_t launch_struct_lists(const StructArgs& a, hipStream_t stream);
 hipError_t launch_importance(const ImpArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream);
+// The 64-key-step forward kernel and the shapes it covers (launch_forward
+// picks it for them).
+bool forward_wide_supported(int dtype, int head_dim, int q_block, int k_block);
+hipError_t launch_forward_wide(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace bsa

@@ -1,0 +1,672 @@
+// Block-sparse attention forward on gfx950 (MI355X): 64-key steps.
+//
+// Pages: "AB-Attention: accurate block-sparse attention for video diffusion"
+// (TL;DR: exact attention only on the selected key/value blocks; key blocks
+// smaller than a tile gathered into full tiles; inverse-inclusion-probability
+// reweighting) and "Attention matrix view: make only frame-0 query rows
+// dense" (sec. 2: a dense row attends to every key/value token).
+//
+// Shape class: bf16 Q/K/V, head_dim 128, 64-row query blocks, key blocks of
+// 16, 32 or 64 keys (the video shapes).  Same results as fwd_kernel up to
+// rounding order; what changes is how one wave spends its issue slots.
+//
+//   * one workgroup = one wave = one (b, h, query block) of 64 rows with the
+//     SIMD's whole register file: Q fragments and the O^T accumulators in
+//     AGPRs, score tiles and softmax state in VGPRs;
+//   * the block's selected keys are walked in 64-key steps (two 32-key
+//     sub-tiles: one 64-key block, or two 32-key / four 16-key blocks
+//     gathered), so the per-step work that does not scale with keys (list
+//     entries, tile addressing, waits, the rescale test) is paid once per
+//     64 MFMAs;
+//   * a step is four phases of 16 MFMAs: S^T(u+1) of each sub-tile (K Q^T),
+//     then O^T += V^T P^T(u) of each sub-tile.  The exponentials of S(u)
+//     run between the first three phases, the row max of S(u+1) in the last;
+//   * K and V fragments stream through one ring of registers, each read
+//     from LDS five fragments ahead of its first MFMA;
+//   * every phase issues the eight DMA loads (HBM/L2 -> LDS, no VGPR
+//     staging) of one 32-key sub-tile into the LDS slot the phase before it
+//     finished reading, so each tile has about two phases to land;
+//   * row sums go to four independent accumulators per query tile, so the
+//     v_dot2 chain never waits on itself; row maxima use v_max3 throughout
+//     (scores are finite or -inf, so no NaN canonicalization is needed).
+#include "fwd_common.h"
+
+namespace bsa {
+namespace {
+
+using namespace fwdc;
+
+constexpr int kSub = 32;     // keys per sub-tile
+constexpr int kNld = 8;      // DMA loads per sub-tile (32 rows x 256 B / 1 KB)
+constexpr int kFetch = 2;    // list loads per step (entry, log-weight)
+constexpr int kRing = 8;     // fragment ring (AGPR quads)
+constexpr int kAhead = 5;    // fragments read ahead of their first MFMA
+constexpr int kLdPer = 1;    // tile loads issued after each of a phase's first MFMAs
+
+// Vector-memory operations issued in a step before its MFMA slot s (s in
+// 0..64): the two list loads at the start, then kLdPer tile loads after each
+// of the first 8 / kLdPer MFMAs of every 16-MFMA phase.
+constexpr int ops_before(int s) {
+  int n = kFetch;
+  for (int p = 0; p < 4; ++p) {
+    const int d = (s - 16 * p) * kLdPer;
+    n += d < 0 ? 0 : (d > kNld ? kNld : d);
+  }
+  return n;
+}
+// the MFMA slot (within its phase) before which all the phase's loads are issued
+constexpr int kLdEnd = kNld / kLdPer;
+// Wait count for the first read of a tile at MFMA slot rs of a step: the
+// tile was issued in phase tp of the same step if its loads (before slot
+// 16 tp + 8) precede rs, else in phase tp of the step before.  Vector-memory
+// operations complete in issue order, so vmcnt(operations issued after the
+// tile's last load) lets the tile land (more loads in flight only make it
+// wait longer).
+constexpr int wait_count(int tp, int rs) {
+  const int per_step = ops_before(64);
+  const int done = ops_before(16 * tp + kLdEnd);
+  return 16 * tp + kLdEnd <= rs ? ops_before(rs) - done : per_step - done + ops_before(rs);
+}
+
+template <int BK>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(1, 1)))
+void fwd_wide_kernel(FwdArgs a) {
+  constexpr int D = 128, QT = 2;
+  constexpr uint32_t RB = D * 2;       // bytes per K/V row
+  constexpr int KC = D / 16;           // k chunks of the Q.K contraction (32x32x16)
+  constexpr int DT = D / 32;           // d tiles of O^T
+  constexpr int KCH = D / 8;           // 16-byte chunks per row
+  constexpr int TILE_E = kSub * D;     // bf16 elements of one sub-tile in LDS
+  constexpr int RPL = 64 / KCH;        // sub-tile rows per load
+  constexpr int NBLK = BK >= kSub ? 1 : kSub / BK;   // key blocks per sub-tile
+  constexpr int PART = kSub / NBLK;                  // keys per part of a sub-tile
+  constexpr int NE = BK >= 64 ? 1 : 64 / BK;         // list entries per step
+  constexpr int G = 4;                               // loads sharing one scalar offset and one M0
+  constexpr float kTau = 8.0f;         // lazy rescale: tolerated growth of the running max (log2)
+  static_assert(PART % (G * RPL) == 0 && kNld == kSub * KCH / 64, "tile shape");
+  static_assert(32 % kRing == 0 && kAhead < kRing, "fragment ring");
+
+  // K sub-tiles of the next step's scores go to K slots 0 / 1, V sub-tiles of
+  // this step's product to V slots 0 / 1.  One LDS array per slot lets the
+  // compiler see which DMA writes a read can depend on.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_E], k_lds1[TILE_E];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_E], v_lds1[TILE_E];
+  // destination of the fast loads of a tile that is loaded separately (a
+  // sub-tile with rows past the sequence or a missing block)
+  __shared__ __attribute__((aligned(16))) uint16_t sink_lds[4 * 64 * 8];
+
+  const int lane = threadIdx.x;
+  const int qc = lane & 31;            // query column of S^T / O^T, key row of the K operand
+  const int hf = lane >> 5;            // k half of the operands, row half of the accumulators
+
+  int bh, qb;
+  if (!schedule(a, blockIdx.x, bh, qb)) return;
+  const int64_t rowid = (int64_t)bh * a.nqb + qb;
+  const int cnt_row = __builtin_amdgcn_readfirstlane(min(max(a.cnt[rowid], 0), a.nkb));
+  const bool part_item = a.split > 1 && (int)blockIdx.x < a.n_dense;
+  const int part = part_item ? (int)blockIdx.x % a.split : 0;
+  const int lo = part_item ? (int)((int64_t)part * cnt_row / a.split) : 0;
+  const int cnt = part_item ? (int)((int64_t)(part + 1) * cnt_row / a.split) - lo : cnt_row;
+  const int nsub = (cnt * BK + kSub - 1) / kSub;     // 32-key sub-tiles of the row
+  const int nsteps = (nsub + 1) / 2;                 // 64-key steps
+
+  const bf16_t* Qb = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)bh * a.seq_alloc * D;
+  const bf16_t* Kb = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)bh * a.seq_alloc * D;
+  const bf16_t* Vb = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)bh * a.seq_alloc * D;
+  const int64_t q0 = (int64_t)qb * 64;
+  const int S32 = (int)a.S;
+  const bool has_w = a.logw != nullptr;
+
+  const uint32_t nbytes = (uint32_t)a.seq_alloc * RB;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)Qb, 0, (int)nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, 0, (int)nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, 0, (int)nbytes, 0x00020000);
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T), rows past S read zeros ----
+  bf16x8 qf[QT][KC];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int64_t row = q0 + 32 * qt + qc;
+    const uint32_t off = row < a.S ? (uint32_t)row * RB + (uint32_t)(16 * hf) : kOob;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[qt][c] = as_frag(Row8<bf16_t>::buf(rq, off + (uint32_t)(32 * c), 0));
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) asm volatile("" : "+a"(qf[qt][c]));
+
+  // ---- list entries of a step: lane b fetches entry b (vector loads, ordered
+  // with the tile loads, so no scalar-cache wait ever holds up LDS reads) ----
+  const uint32_t lbytes = (uint32_t)(a.nkb - lo) * 4u;
+  const int64_t lbase = rowid * a.nkb + lo;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.idx + lbase), 0, (int)lbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(has_w ? (void*)(a.logw + lbase) : (void*)(a.idx + lbase), 0,
+                                        (int)lbytes, 0x00020000);
+  struct Raw {
+    int j;   // lane b < NE: list entry b of the step
+    int w;   // its log-weight bits
+  };
+  // Sub-tile h of a step, part b: first key, valid keys, log2-domain weight.
+  struct Info {
+    int key0[2][NBLK];
+    int valid[2][NBLK];
+    float bias[2][NBLK];
+  };
+  auto fetch = [&](int u) {
+    Raw r;
+    if constexpr (NE == 1) {   // one entry for all lanes: a scalar offset
+      const uint32_t off = min((uint32_t)u, (uint32_t)max(cnt - 1, 0)) * 4u;
+      r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, 0, (int)off, 0);
+      r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, 0, (int)off, 0);
+    } else {
+      const int b = lane < NE ? lane : 0;
+      const uint32_t off = min((uint32_t)(u * NE + b), (uint32_t)max(cnt - 1, 0)) * 4u;
+      r.j = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)off, 0, 0);
+      r.w = (int)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+    }
+    return r;
+  };
+  auto info = [&](int u, const Raw& r) {
+    Info si;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) {
+        const int e = NE == 1 ? 0 : h * NBLK + b;        // entry of the step
+        const int pos = u * NE + e;
+        const int jr = NE == 1 ? __builtin_amdgcn_readfirstlane(r.j) : __builtin_amdgcn_readlane(r.j, e);
+        const bool ok = pos < cnt && (uint32_t)jr < (uint32_t)a.nkb;
+        const int key0 = jr * BK + (NE == 1 ? h * kSub : 0);
+        si.key0[h][b] = ok ? key0 : 0;
+        const int rest = S32 - key0;
+        si.valid[h][b] = ok ? (rest < PART ? (rest > 0 ? rest : 0) : PART) : 0;
+        const int wb = NE == 1 ? __builtin_amdgcn_readfirstlane(r.w) : __builtin_amdgcn_readlane(r.w, e);
+        const float w = has_w ? __builtin_bit_cast(float, wb) : 0.0f;
+        si.bias[h][b] = ok ? w * 1.4426950408889634f : 0.0f;
+      }
+    }
+    return si;
+  };
+  auto is_full = [&](const Info& si, int h) {
+    bool full = true;
+#pragma unroll
+    for (int p = 0; p < NBLK; ++p) full = full && si.valid[h][p] == PART;
+    return full;
+  };
+
+  // ---- sub-tile -> LDS slot by DMA ----
+  // Load n of this lane fills LDS chunk n*64 + lane of the slot: tile row
+  // r = n*RPL + lane/KCH, holding logical chunk (lane % KCH) ^ swizzle(r).
+  // K rows are read back as 16-byte A-operand pieces (16 consecutive rows at
+  // one logical chunk): swizzle r & 15.  V rows are read with the transposing
+  // 8-byte load (4 rows x 4 chunks per 16 lanes): swizzle 4 (r & 3).
+  const int vrow = lane / KCH;
+  auto chunk_off = [&](int n, bool is_k) {
+    const int r = n * RPL + vrow;
+    return (uint32_t)(vrow * D + ((lane % KCH) ^ (is_k ? (r & 15) : swz_v<D>(r))) * 8) * 2;
+  };
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  auto kslot = [&](int s) { return s == 0 ? (lds_u16*)k_lds0 : (lds_u16*)k_lds1; };
+  auto vslot = [&](int s) { return s == 0 ? (lds_u16*)v_lds0 : (lds_u16*)v_lds1; };
+  // load n of a full sub-tile, or the same load into the sink (redirect).
+  // The immediate offset moves both the global and the LDS address, so the
+  // G loads of a group share one scalar offset and one M0.
+  auto load_fast = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, int h, lds_u16* dst, bool is_k, int n,
+                       bool redirect) {
+    const int g0 = (n / G) * G;
+    const int p = (g0 * RPL) / PART;
+    const int r0 = g0 * RPL - p * PART;
+    const uint32_t so = ((uint32_t)si.key0[h][p] + (uint32_t)r0) * RB;
+    lds_u16* d = redirect ? (lds_u16*)sink_lds : dst + g0 * 64 * 8;
+    auto* ld = (__attribute__((address_space(3))) void*)d;
+    const int vo = (int)chunk_off(n, is_k);
+    switch (n % G) {
+      case 0: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 0, 0); break;
+      case 1: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 1024, 0); break;
+      case 2: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 2048, 0); break;
+      default: __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, ld, 16, vo, (int)so, 3072, 0); break;
+    }
+  };
+  // a sub-tile with missing keys: per-lane offsets, rows past the valid keys
+  // read zeros (so V rows past the sequence never reach O as NaN)
+  auto load_slow = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, int h, lds_u16* dst, bool is_k) {
+#pragma unroll
+    for (int n = 0; n < kNld; ++n) {
+      const int p = (n * RPL) / PART;
+      const int r0 = n * RPL - p * PART;
+      const uint32_t so = ((uint32_t)si.key0[h][p] + (uint32_t)r0) * RB;
+      const uint32_t vo = vrow < si.valid[h][p] - r0 ? chunk_off(n, is_k) + so : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + n * 64 * 8), 16, (int)vo, 0, 0, 0);
+    }
+  };
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rsrc, const Info& si, int h, lds_u16* dst, bool is_k) {
+    if (is_full(si, h)) {
+#pragma unroll
+      for (int n = 0; n < kNld; ++n) load_fast(rsrc, si, h, dst, is_k, n, false);
+    } else {
+      load_slow(rsrc, si, h, dst, is_k);
+    }
+  };
+
+  // ---- fragments ----
+  // K A-operand of chunk c: tile row qc, logical chunk 2c + hf: ka ^ (c * 32).
+  // V^T A-operand of d tile dt, key chunk c: two transposing reads, lane i of
+  // 16-lane group g at tile row 16c + 4hf + i/4 (+ 8), columns
+  // 32dt + 16(g & 1) + 4(i & 3): va ^ (dt * 64) + 16c rows.
+  const uint32_t ka = (uint32_t)(qc * KCH * 16) | (uint32_t)((hf ^ (qc & 15)) * 16);
+  const uint32_t va = [&] {
+    const int i = lane & 15, g = lane >> 4;
+    const int r = 4 * hf + (i >> 2);
+    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
+    return (uint32_t)(r * D * 2) | (uint32_t)((lc ^ swz_v<D>(r)) * 16) | (uint32_t)((i & 1) * 8);
+  }();
+  // fragment x of a step (0..31): x < 16 the K fragment (sub-tile x / 8,
+  // chunk x % 8) of the next step's scores; x >= 16 the V fragment (sub-tile
+  // f / 8, key chunk (f % 8) / 4, d tile f % 4), f = x - 16, of this step's product
+  auto read_frag = [&](int x) {
+    if (x < 16) {
+      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(x / 8));
+      const u32x4 v = *reinterpret_cast<const lds_u32x4*>(kt + (ka ^ (uint32_t)((x % 8) * 32)));
+      return as_frag(make_uint4(v[0], v[1], v[2], v[3]));
+    }
+    const int f = x - 16;
+    const int c = (f % 8) / 4, dt = f % 4;
+    const lds_u8* vp = reinterpret_cast<const lds_u8*>(vslot(f / 8)) + (va ^ (uint32_t)(dt * 64)) + (16 * c) * D * 2;
+    const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp));
+    const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp + 8 * D * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // accumulator register r of this lane is tile row 8*(r/4) + 4*hf + r%4
+  auto mask = [&](f32x16 (&s)[QT], const Info& si, int h) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+      const int p = row / PART;
+      const int v = p == 0 ? si.valid[h][0] : si.valid[h][NBLK - 1];
+      const bool bad = row - p * PART >= v;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        if (bad) s[qt][r] = -INFINITY;
+    }
+  };
+
+  float m_run[QT], thr[QT];
+  float lp[QT][4];                     // row sum in four independent parts
+  f32x16 o[QT][DT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    thr[qt] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lp[qt][i] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
+  }
+
+  // Row max (log2 domain, scale and weights applied) of a step's scores:
+  // the lane's 32 keys per query tile in four groups of 8 (sub-tile h,
+  // register half e: the parts of 16-key blocks), then the weights, then
+  // lane ^ 32.  Stage g < 4 reduces group g; stage 4 combines.
+  auto rowmax_stage = [&](const f32x16 (&s)[2][QT], const Info& si, float (&pm)[QT][4], float (&mx)[QT], int g) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      if (g < 4) {
+        const f32x16& x = s[g / 2][qt];
+        const int r = 8 * (g % 2);
+        pm[qt][g] = max3(max3(x[r], x[r + 1], x[r + 2]), max3(x[r + 3], x[r + 4], x[r + 5]), max3(x[r + 6], x[r + 7], x[r + 7]));
+        pin_before(pm[qt][g]);
+      } else {
+        float m;
+        if constexpr (NE == 1) {
+          m = max3(max3(pm[qt][0], pm[qt][1], pm[qt][2]), pm[qt][3], pm[qt][3]) * a.scale_log2 + si.bias[0][0];
+        } else if constexpr (NBLK == 1) {
+          const float m0 = max3(pm[qt][0], pm[qt][1], pm[qt][1]) * a.scale_log2 + si.bias[0][0];
+          const float m1 = max3(pm[qt][2], pm[qt][3], pm[qt][3]) * a.scale_log2 + si.bias[1][0];
+          m = max3(m0, m1, m1);
+        } else {
+          const float m0 = pm[qt][0] * a.scale_log2 + si.bias[0][0], m1 = pm[qt][1] * a.scale_log2 + si.bias[0][1];
+          const float m2 = pm[qt][2] * a.scale_log2 + si.bias[1][0], m3 = pm[qt][3] * a.scale_log2 + si.bias[1][1];
+          m = max3(max3(m0, m1, m2), m3, m3);
+        }
+        // with lane ^ 32 (one v_permlane32_swap), no NaN canonicalization
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        mx[qt] = max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        pin_before(mx[qt]);
+      }
+    }
+  };
+  auto rowmax_full = [&](const f32x16 (&s)[2][QT], const Info& si, float (&mx)[QT]) {
+    float pm[QT][4];
+#pragma unroll
+    for (int g = 0; g < 5; ++g) rowmax_stage(s, si, pm, mx, g);
+  };
+
+  // vector reads of O 12+ wait states after the last P V MFMA
+  auto fence_o = [&]() {
+    asm volatile("s_nop 11" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[qt][dt]));
+  };
+  // lazy rescale: the reference max moves only when a row max grows past
+  // m_run + kTau (so every p <= 2^kTau); O and the row sums follow it
+  auto rescale = [&](const float (&mx)[QT]) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float m_new = mx[qt] > thr[qt] ? mx[qt] : m_run[qt];
+      const float alpha = fast_exp2(m_run[qt] - (m_new == -INFINITY ? 0.0f : m_new));
+      m_run[qt] = m_new;
+      thr[qt] = m_new + kTau;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lp[qt][i] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[qt][dt] *= alpha;
+        asm volatile("" : "+a"(o[qt][dt]));   // one tile at a time in vector registers
+      }
+    }
+  };
+
+  auto tile_wait = [&](auto n) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory"); };
+
+  if (nsteps > 0) {
+    f32x16 sc[2][2][QT];      // [buffer][sub-tile][query tile]: S of steps u (buffer u&1) and u+1
+    bf16x8 ring[kRing];       // K / V fragments in flight
+    Info i_u = info(0, fetch(0));
+    Info i_u1 = info(1, fetch(1));
+    Info i_u2 = info(2, fetch(2));
+    Raw r3 = fetch(3);
+    Raw r4 = fetch(4);
+
+    // ---- prologue: S(0) from K sub-tiles 0, 1; K of step 1 and V(0, 0) in flight ----
+    load_tile(rk, i_u, 0, kslot(0), true);
+    load_tile(rk, i_u, 1, kslot(1), true);
+    load_tile(rv, i_u, 0, vslot(0), false);
+    asm volatile("s_waitcnt vmcnt(%0)\n s_nop 1" ::"n"(2 * kNld) : "memory");   // K(0, 0) landed
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNld) : "memory");   // K(0, 1) landed
+      const lds_u8* kt = reinterpret_cast<const lds_u8*>(kslot(h));
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 v = *reinterpret_cast<const lds_u32x4*>(kt + (ka ^ (uint32_t)(c * 32)));
+        const bf16x8 kf = as_frag(make_uint4(v[0], v[1], v[2], v[3]));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          if (c == 0) mma_s_first(sc[0][h][qt], kf, qf[qt][c]);
+          else mma_s(sc[0][h][qt], kf, qf[qt][c]);
+        }
+      }
+    }
+    // the reads of K slots 0 and 1 are complete (each MFMA waited for its
+    // fragment): K of step 1 goes there
+    load_tile(rk, i_u1, 0, kslot(0), true);
+    load_tile(rk, i_u1, 1, kslot(1), true);
+    asm volatile("s_nop 11" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(sc[0][h][qt]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (!is_full(i_u, h)) mask(sc[0][h], i_u, h);
+    {
+      float mx[QT];
+      rowmax_full(sc[0], i_u, mx);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {   // first reference max: O and the sums are still 0
+        m_run[qt] = mx[qt];
+        thr[qt] = mx[qt] + kTau;
+      }
+    }
+    // every prologue load has landed before the loop (the in-loop wait counts
+    // assume the steady-state order of loads)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < kAhead; ++x) ring[x % kRing] = read_frag(x);
+
+    // ---- one 64-key step ----
+    // Step u (p = u & 1): sc[p] holds S(u) (masked, its max folded into
+    // m_run); K slots hold the sub-tiles of step u+1, V slot 0 holds V(u, 0).
+    //   phase 0 (MFMA slots 0..15):  S(u+1, 0) = K(u+1, 0) Q^T; loads V(u, 1) -> V slot 1
+    //   phase 1 (16..31):            S(u+1, 1);                loads K(u+2, 0) -> K slot 0
+    //   phase 2 (32..47):            O += V(u, 0)^T P(u, 0)^T; loads K(u+2, 1) -> K slot 1
+    //   phase 3 (48..63):            O += V(u, 1)^T P(u, 1)^T; loads V(u+1, 0) -> V slot 0
+    // The exponentials of S(u) run in phases 0-2 (P(u, 0) complete before
+    // phase 2, P(u, 1) before its second key chunk), the row max of S(u+1)
+    // in phase 3; then the rescale test.
+    auto step = [&](auto par, int u) {
+      constexpr int p = decltype(par)::value;
+      f32x16 (&scur)[2][QT] = sc[p];
+      f32x16 (&snext)[2][QT] = sc[p ^ 1];
+      Raw r5 = fetch(u + 5);
+
+      // whether each phase's tile (V(u, 1), K(u+2, 0), K(u+2, 1), V(u+1, 0))
+      // has missing keys and takes the slow path
+      const bool slow[4] = {!is_full(i_u, 1), !is_full(i_u2, 0), !is_full(i_u2, 1), !is_full(i_u1, 0)};
+
+      // softmax offsets of S(u): weight of each part minus the reference max
+      // (a row with no valid key yet has only -inf scores: offset 0)
+      float off[QT][2][NBLK];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int b = 0; b < NBLK; ++b) off[qt][h][b] = i_u.bias[h][b] - mu;
+      }
+
+      // P(u) as bf16: pw[h][qt][k] packs keys 2k, 2k+1 of the lane's half of sub-tile h
+      uint32_t pw[2][QT][8];
+      // exponential pair k of sub-tile h, both query tiles; the row sum adds
+      // exactly the bf16 values the P V product uses
+      auto pair = [&](int h, int k) {
+        const int b = (2 * k < 8) ? 0 : NBLK - 1;
+        float p0[QT], p1[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) pin_after(off[qt][h][b]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          p0[qt] = scur[h][qt][2 * k] * a.scale_log2 + off[qt][h][b];
+          p1[qt] = scur[h][qt][2 * k + 1] * a.scale_log2 + off[qt][h][b];
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          p0[qt] = fast_exp2(p0[qt]);
+          p1[qt] = fast_exp2(p1[qt]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) pw[h][qt][k] = pack_bf16x2(p0[qt], p1[qt]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          float& l = lp[qt][k & 3];
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[h][qt][k]), kOnes2, l, false);
+          pin_before(pw[h][qt][k]);
+          pin_before(l);
+        }
+      };
+
+      float mx[QT], pm[QT][4];
+      static_for<0, 64>([&](auto slot) {
+        constexpr int s = decltype(slot)::value;
+        constexpr int ph = s / 16, i = s % 16;
+        if constexpr (i == 0 && (ph == 2 || ph == 3)) asm volatile("s_nop 1" ::: "memory");   // P writes -> MFMA reads
+        if constexpr (s == 48) {
+          // S(u+1) complete (16+ MFMAs ago): mask its partial sub-tiles
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) asm volatile("" : "+v"(snext[h][qt]));
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (!is_full(i_u1, h)) mask(snext[h], i_u1, h);
+        }
+        if constexpr (i == 0) {
+          // a tile with missing keys is loaded now by the slow path; the
+          // phase's interleaved loads then go to the sink
+          if (slow[ph]) {
+            if constexpr (ph == 0) load_slow(rv, i_u, 1, vslot(1), false);
+            if constexpr (ph == 1) load_slow(rk, i_u2, 0, kslot(0), true);
+            if constexpr (ph == 2) load_slow(rk, i_u2, 1, kslot(1), true);
+            if constexpr (ph == 3) load_slow(rv, i_u1, 0, vslot(0), false);
+          }
+        }
+        // fragment read kAhead fragments ahead of fragment s / 2
+        if constexpr ((s & 1) == 0) {
+          constexpr int x = s / 2 + kAhead;   // >= 32: the next step's K fragments
+          constexpr int xr = x % 32;
+          // first read of a tile: wait for its loads
+          // (K slot 0 <- phase 1, K slot 1 <- phase 2, V slot 0 <- phase 3, V slot 1 <- phase 0)
+          if constexpr (xr == 0) tile_wait(std::integral_constant<int, wait_count(1, s)>{});
+          if constexpr (xr == 8) tile_wait(std::integral_constant<int, wait_count(2, s)>{});
+          if constexpr (xr == 16) tile_wait(std::integral_constant<int, wait_count(3, s)>{});
+          if constexpr (xr == 24) tile_wait(std::integral_constant<int, wait_count(0, s)>{});
+          ring[x % kRing] = read_frag(xr);
+        }
+        // the MFMA of slot s
+        if constexpr (s < 32) {
+          constexpr int h = s / 16, c = (s % 16) / 2, qt = s % 2;
+          if constexpr (c == 0) mma_s_first(snext[h][qt], ring[(s / 2) % kRing], qf[qt][c]);
+          else mma_s(snext[h][qt], ring[(s / 2) % kRing], qf[qt][c]);
+        } else {
+          constexpr int f = (s - 32) / 2, qt = s % 2;
+          constexpr int h = f / 8, c = (f % 8) / 4, dt = f % 4;
+          const bf16x8 pb = as_frag(make_uint4(pw[h][qt][4 * c], pw[h][qt][4 * c + 1], pw[h][qt][4 * c + 2],
+                                               pw[h][qt][4 * c + 3]));
+          mma_o(o[qt][dt], ring[(s / 2) % kRing], pb);
+        }
+        // the phase's tile loads, kLdPer after each of its first MFMAs
+        if constexpr (i < kLdEnd) {
+#pragma unroll
+          for (int n = i * kLdPer; n < (i + 1) * kLdPer; ++n) {
+            if constexpr (ph == 0) load_fast(rv, i_u, 1, vslot(1), false, n, slow[0]);
+            if constexpr (ph == 1) load_fast(rk, i_u2, 0, kslot(0), true, n, slow[1]);
+            if constexpr (ph == 2) load_fast(rk, i_u2, 1, kslot(1), true, n, slow[2]);
+            if constexpr (ph == 3) load_fast(rv, i_u1, 0, vslot(0), false, n, slow[3]);
+          }
+        }
+        // exponential pairs of S(u): (0, 0..5) in phase 0, (0, 6..7) and
+        // (1, 0..3) in phase 1, (1, 4..7) in phase 2
+        constexpr int unit = s == 0 ? 0 : s == 3 ? 1 : s == 6 ? 2 : s == 8 ? 3 : s == 11 ? 4 : s == 13 ? 5
+                           : s == 16 ? 6 : s == 18 ? 7 : s == 21 ? 8 : s == 24 ? 9 : s == 26 ? 10 : s == 29 ? 11
+                           : s == 32 ? 12 : s == 35 ? 13 : s == 38 ? 14 : s == 41 ? 15 : -1;
+        if constexpr (unit >= 0) pair(unit / 8, unit % 8);
+        // row max of S(u+1) over phase 3
+        if constexpr (s >= 48 && (s - 48) % 3 == 0 && (s - 48) / 3 < 5) rowmax_stage(snext, i_u1, pm, mx, (s - 48) / 3);
+      });
+
+      if (u + 1 < nsteps) {
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > thr[qt];
+        if (__any(grow)) {
+          fence_o();
+          rescale(mx);
+        }
+      }
+      i_u = i_u1;
+      i_u1 = i_u2;
+      i_u2 = info(u + 3, r3);
+      r3 = r4;
+      r4 = r5;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    for (int u = 0; u < nsteps; u += 2) {
+      step(I0{}, u);
+      if (u + 1 < nsteps) step(I1{}, u + 1);
+    }
+  }
+  fence_o();
+  // the last steps' loads must land before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
+  float* ostage = reinterpret_cast<float*>(k_lds0);
+  bf16_t* Ob = reinterpret_cast<bf16_t*>(a.out) + (int64_t)bh * a.seq_alloc * D;
+  constexpr int QB = 64;
+  float* wsO = part_item ? a.ws + (int64_t)blockIdx.x * QB * D : nullptr;
+  float* wsM = part_item ? a.ws + (int64_t)a.n_dense * QB * D + (int64_t)blockIdx.x * QB : nullptr;
+  float* wsL = part_item ? wsM + (int64_t)a.n_dense * QB : nullptr;
+  constexpr int C8 = D / 8;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l = add_xor32((lp[qt][0] + lp[qt][1]) + (lp[qt][2] + lp[qt][3]));
+    const float inv = part_item ? 1.0f : (l > 0.0f ? 1.0f / l : 0.0f);
+    const int64_t qrow0 = q0 + 32 * qt;
+    if (part_item) {
+      if (hf == 0) {
+        wsM[32 * qt + qc] = m_run[qt];
+        wsL[32 * qt + qc] = l;
+      }
+    } else if (hf == 0 && a.lse) {
+      const int64_t row = qrow0 + qc;
+      const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
+      if (row < a.seq_alloc)
+        a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
+      if ((qc >> 4) == half) {
+        const int q = qc & 15;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x16 t = o[qt][dt];
+          asm volatile("" : "+v"(t));   // one tile in vector registers at a time
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int ch = 8 * dt + 2 * r4 + hf;
+            *reinterpret_cast<f32x4*>(ostage + q * D + ((ch ^ q) * 4)) =
+                f32x4{t[4 * r4], t[4 * r4 + 1], t[4 * r4 + 2], t[4 * r4 + 3]} * inv;
+          }
+        }
+      }
+      for (int e = lane; e < 16 * C8; e += 64) {
+        const int q = e / C8, c8 = e % C8;
+        const int64_t row = qrow0 + 16 * half + q;
+        if (row >= a.seq_alloc) continue;
+        float v[8];
+        if (row < a.S) {
+          const float4 x = *reinterpret_cast<const float4*>(ostage + q * D + (((2 * c8) ^ q) * 4));
+          const float4 y = *reinterpret_cast<const float4*>(ostage + q * D + (((2 * c8 + 1) ^ q) * 4));
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+          v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = 0.0f;
+        }
+        if (part_item) store8<float>(wsO + (row - q0) * D + c8 * 8, v);
+        else store8<bf16_t>(Ob + row * D + c8 * 8, v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// The 64-key-step forward covers bf16, head_dim 128, 64-row query blocks.
+bool forward_wide_supported(int dtype, int head_dim, int q_block, int k_block) {
+  return dtype == 0 && head_dim == 128 && q_block == 64 && (k_block == 16 || k_block == 32 || k_block == 64);
+}
+
+hipError_t launch_forward_wide(const FwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)forward_grid(a)), block(64);
+  switch (a.k_block) {
+    case 16: hipLaunchKernelGGL((fwd_wide_kernel<16>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((fwd_wide_kernel<32>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((fwd_wide_kernel<64>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsa
