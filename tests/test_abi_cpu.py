@@ -284,3 +284,43 @@ def test_dense_split_suggestion():
     assert bsa.suggest_dense_split(g, c, simds=1024) == 1
     g = bsa.Geometry(1, 2, 64, 0, 0, 0, 64, 32, 32, 64)    # text only: no frame-0 rows
     assert bsa.suggest_dense_split(g, torch.full((1, 2, 2), 2, dtype=torch.int32), simds=1024) == 1
+
+
+def test_validation_under_host_sanitizers(tmp_path):
+    """Every validation path of the C ABI, plus the host-only bsa_derive and
+    bsa_classify_heads, driven by a plain C program (tests/c_abi/bsa_validate.c)
+    against abi.cpp rebuilt with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host code (device code is built as usual).  No call reaches a
+    launch, so no GPU is needed; any sanitizer report fails the run."""
+    import subprocess
+    from block_sparse_attention_42_amd import build as B
+    objs = [os.path.join(B.OBJ, s + ".o") for s in B.SOURCES if s != "abi.cpp"]
+    if not all(os.path.exists(o) for o in objs) or not os.path.exists(B.HIPCC):
+        pytest.skip("library objects not built")
+    clang = "/opt/rocm/llvm/bin/clang"
+    if not os.path.exists(clang):
+        pytest.skip("no clang")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+    host_san = [f for s in san[:2] for f in ("-Xarch_host", s)] + ["-fno-omit-frame-pointer", "-g"]
+    inc = os.path.join(ROOT, "include")
+    abi_o = str(tmp_path / "abi_san.o")
+    cmd = [B.HIPCC, *B.COMMON, *B.EXTRA["abi.cpp"], *host_san, "-c", os.path.join(B.CSRC, "abi.cpp"), "-o", abi_o]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    syms = subprocess.run(["nm", "-u", abi_o], capture_output=True, text=True).stdout
+    assert "__asan_report_load" in syms and "__ubsan_handle_" in syms, "host code not instrumented"
+    drv_o = str(tmp_path / "validate.o")
+    r = subprocess.run([clang, "-std=c99", "-Wall", "-Werror", "-O1", *san, "-I", inc, "-c",
+                        os.path.join(ROOT, "tests", "c_abi", "bsa_validate.c"), "-o", drv_o],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    exe = str(tmp_path / "bsa_validate")
+    r = subprocess.run([clang + "++", *san, drv_o, abi_o, *objs, "-L/opt/rocm/lib", "-lamdhip64",
+                        "-Wl,-rpath,/opt/rocm/lib", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:exitcode=86",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1:exitcode=87")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, (r.returncode, r.stdout[-2000:], r.stderr[-4000:])
+    assert "all validation checks passed" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
