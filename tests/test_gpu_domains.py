@@ -114,11 +114,15 @@ def test_domains_two_batch_elements_and_forward(domain):
     og = geometry_of(w)
     o = out.float().cpu().numpy()
     ch, ih = cnt.cpu().numpy(), idx.cpu().numpy()
+    errs = []
     for b in range(og.B):
         for h in range(og.H):
             ref, _ = oracle.attention_head(q[b, h], k[b, h], v[b, h], og, ch[b, h], ih[b, h],
                                            np.zeros((og.nqb, og.nkb), np.float32))
-            assert np.abs(o[b, h, :ref.shape[0]] - ref).max() <= 2e-2
+            err = np.abs(o[b, h, :ref.shape[0]] - ref)
+            assert err.max() <= 2e-2
+            errs.append(err.ravel())
+    assert np.concatenate(errs).mean() <= 2e-3
 
 
 def test_eg_routing_full_size():

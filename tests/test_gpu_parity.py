@@ -163,8 +163,15 @@ def test_small_workloads_every_row(name):
 FULL = ["wan_1p3b_keep10", "wan_1p3b_sampled_k16", "hunyuan_keep08"]
 
 
+# whole heads whose every row's mask, count, list (and log-weights) are
+# compared at full size: all heads of the headline workload, four elsewhere
+WHOLE_HEADS = {"wan_1p3b_keep10": None, "wan_1p3b_sampled_k16": 4, "hunyuan_keep08": 4}
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_rows(name):
+    """Full size: masks and lists of every row of whole heads (top-k mask first,
+    frame-0 rows overwritten after), outputs on sampled rows."""
     w = W.workload(name)
     g = geometry_of(w)
     q, k, v = inputs_of(w)
@@ -174,12 +181,21 @@ def test_full_size_sampled_rows(name):
     assert np.array_equal(r["qp"], oqp) and np.array_equal(r["kp"], okp)
     rng = np.random.default_rng(1)
     f0 = list(g.frame0_q_blocks())
+    nh = WHOLE_HEADS[name]
+    heads = list(range(g.H)) if nh is None else sorted(set([0, g.H - 1] + rng.choice(np.arange(1, g.H - 1), nh - 2,
+                                                                                      replace=False).tolist()))
+    every = [(0, h, i) for h in heads for i in range(g.nqb)]
+    _say(f"    lists of every row of heads {heads} ({len(every)} rows)")
+    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w), rows=every)
+    _check_lists(w, r, om, ocnt, oidx, ologw, every)
+    # output rows: the first, last and a few random heads, a sample of their rows
     rows = []
     for h in sorted(set([0, g.H - 1] + rng.integers(0, g.H, 2).tolist())):
         picks = {f0[0], f0[-1], f0[-1] + 1, g.nqb - 1, g.nqb // 2} | set(rng.integers(0, g.nqb, 6).tolist())
         rows += [(0, h, i) for i in sorted(picks)]
-    om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w), rows=rows)
-    _check_lists(w, r, om, ocnt, oidx, ologw, rows)
+    if any(h not in heads for (_, h, _) in rows):
+        om, ocnt, oidx, ologw = oracle.build_mask(oqp, okp, g, params_of(w), rows=rows + every)
+        _check_lists(w, r, om, ocnt, oidx, ologw, rows)
     # every row non-empty, every list ascending (a property that holds at any size)
     assert (r["cnt"] >= 1).all()
     if w.mode == "topk":

@@ -136,11 +136,15 @@ def test_frame_scores_labels_and_forward(name, window):
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     ch, ih = cnt.cpu().numpy(), idx.cpu().numpy()
+    errs = []
     for b in range(og.B):
         for h in range(og.H):
             ref, _ = oracle.attention_head(q[b, h], k[b, h], v[b, h], og, ch[b, h], ih[b, h],
                                            np.zeros((og.nqb, og.nkb), np.float32))
-            assert np.abs(o[b, h, :ref.shape[0]] - ref).max() <= 2e-2   # float32 inputs are rounded to bf16 on the GPU
+            err = np.abs(o[b, h, :ref.shape[0]] - ref)
+            assert err.max() <= 2e-2
+            errs.append(err.ravel())
+    assert np.concatenate(errs).mean() <= 2e-3
 
 
 def test_lists_full_size():
