@@ -1,6 +1,6 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
-One step = the whole path on one batch: pool Q, pool K, build the mask
+One step = the whole path on one batch: pool Q and K (one launch), build the mask
 (logits, per-row top-k or sampling, overrides, lists), sparse forward.
 Inputs are resident in HBM before the timed region.  Prints one JSON line.
 
@@ -11,7 +11,10 @@ executed blocks (4 * D * q_block * k_block per selected block) divided by
 the step time.  The forward alone (the dominant kernel) is reported in
 `roofline` and `fwd_*`, timed with HIP events on the launch stream:
 `fwd_ms_per_call` is the median over the timed steps, `roofline.achieved`
-uses the mean launch duration.
+uses the mean launch duration.  After the headline workload, `configs` holds
+the same figures for the other workloads (tiny f32 clip, 5-frame clip,
+sampled 16-key blocks, HunyuanVideo-sized clip with text), timed the same
+way over fewer steps.
 """
 import argparse
 import hashlib
@@ -48,45 +51,49 @@ def _args():
     ap.add_argument("--dense-split", default="auto",
                     help="key split of the frame-0 rows in the forward: a number 1..16, or auto "
                          "(suggest_dense_split from the lists, chosen before the timed steps)")
+    ap.add_argument("--configs", default="all",
+                    help="the other workloads measured after the headline: all, none, or a comma list")
+    ap.add_argument("--config-steps", type=int, default=20)
+    ap.add_argument("--config-warmup", type=int, default=5)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
 
 
-def code_digest(path_src):
-    """sha256 of a HIP source with `//` comments and blank lines removed, plus
-    its compile flags (the code the counters measured)."""
+FWD_SOURCES = ("forward.hip", "forward_wide.hip", "fwd_common.h")
+
+
+def fwd_kernel_of(w):
+    """The forward kernel a workload runs: the 64-key-step kernel for bf16,
+    head_dim 128, 64-row query blocks; the general kernel otherwise."""
+    wide = w.dtype == "bf16" and w.D == 128 and w.q_block == 64 and w.k_block in (16, 32, 64)
+    return "fwd_wide_kernel" if wide else "fwd_kernel"
+
+
+def code_digest(names=FWD_SOURCES):
+    """sha256 of the forward's HIP sources with `//` comments and blank lines
+    removed, plus their compile flags (the code the counters measured)."""
     from block_sparse_attention_42_amd.build import COMMON, EXTRA
     out = []
-    for line in open(path_src, encoding="utf-8"):
-        code = line.split("//", 1)[0].rstrip()
-        if code:
-            out.append(code)
-    out.append(" ".join(COMMON + EXTRA.get(os.path.basename(path_src), [])))
+    for name in names:
+        for line in open(os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", name), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                out.append(code)
+        out.append(" ".join(COMMON + EXTRA.get(name, [])))
     return hashlib.sha256("\n".join(out).encode()).hexdigest()
 
 
-def _traffic(path_src, name):
-    """HBM bytes per forward launch from committed rocprofv3 counters, if the kernel code is unchanged."""
-    f = os.path.join(ROOT, "profiles", f"traffic_fwd_{name}.json")
+def _profile_record(kind, kernel, name, field):
+    """A figure from a committed rocprofv3 record (profiles/<kind>_<kernel>_<workload>.json),
+    if the forward's code is unchanged since the counters were taken."""
+    f = os.path.join(ROOT, "profiles", f"{kind}_{kernel}_{name}.json")
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
-    if rec.get("forward_hip_code_sha256") != code_digest(path_src):
+    if rec.get("forward_code_sha256") != code_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
-
-
-def _mfma_busy(path_src, name):
-    """The forward's matrix-core busy fraction from the committed rocprofv3 SQ
-    counters, if the kernel code is unchanged."""
-    f = os.path.join(ROOT, "profiles", f"sq_fwd_{name}.json")
-    if not os.path.exists(f):
-        return None
-    rec = json.load(open(f))
-    if rec.get("forward_hip_code_sha256") != code_digest(path_src):
-        return None
-    return rec.get("mfma_busy_frac")
+    return rec.get(field)
 
 
 def cpu_baseline(w, q, k, v, nblocks, nheads):
@@ -317,6 +324,131 @@ def graph_timing(torch, step, stream, ev, steps, out):
     return {"ms_per_step": round(ms, 4), "replay_identical_to_eager": same}
 
 
+class PathRun:
+    """The hot path on one workload: inputs resident on the GPU, output
+    buffers allocated once, the key split of the frame-0 rows chosen from the
+    lists after warmup; `timed(steps)` times whole steps and each stage."""
+
+    def __init__(self, bsa, torch, w, warmup, dense_split="auto", keep_host=False):
+        import workloads as W
+        self.bsa, self.torch, self.w = bsa, torch, w
+        t_gen = time.perf_counter()
+        q, k, v = W.generate(w)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = torch.device("cuda:0")
+        self.qd, self.kd, self.vd = (torch.from_numpy(x).to(dt).to(dev) for x in (q, k, v))
+        if keep_host:
+            if w.dtype == "bf16":     # what the oracle sees: the bf16 values
+                q, k, v = (t.float().cpu().numpy() for t in (self.qd, self.kd, self.vd))
+            self.host = (q, k, v)
+        del q, k, v
+        self.input_gen_s = time.perf_counter() - t_gen
+        self.g = g = bsa.Geometry(w.B, w.H, w.text_len, w.frames, w.latent_h, w.latent_w, w.D, w.q_block,
+                                  w.k_block, w.seq_alloc)
+        self.p = bsa.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio, frame0_dense=w.frame0_dense,
+                                text_columns=w.text_columns, log_cluster=w.log_cluster, seed=w.sample_seed)
+        d = bsa.bsa_derive(g, self.p)
+        self.nqb, self.nkb = nqb, nkb = d["nqb"], d["nkb"]
+        self.qp = torch.empty((w.B, w.H, nqb, w.D), dtype=torch.float32, device=dev)
+        self.kp = torch.empty((w.B, w.H, nkb, w.D), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.uint8, device=dev)
+        self.cnt = torch.empty((w.B, w.H, nqb), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.int32, device=dev)
+        self.logw = (torch.empty((w.B, w.H, nqb, nkb), dtype=torch.float32, device=dev)
+                     if w.mode == "sample" else None)
+        self.out = torch.empty_like(self.qd)
+        self.stream = torch.cuda.current_stream()
+        self.split, self.ws = 1, None
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        # the key split of the frame-0 rows: chosen from the lists, outside the timed region
+        split = bsa.suggest_dense_split(g, self.cnt) if dense_split == "auto" else int(dense_split)
+        if split != 1:
+            self.split = split
+            self.ws = torch.empty(max(bsa.bsa_forward_split_workspace_bytes(g, split), 16), dtype=torch.uint8,
+                                  device=dev)
+            for _ in range(2):
+                self.step()
+            torch.cuda.synchronize()
+        self.blocks = int(self.cnt.sum().item())
+        self.flops = 4.0 * w.D * w.q_block * w.k_block * self.blocks
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def step(self, times=None):
+        bsa, g, s = self.bsa, self.g, self.stream
+        e = [self.ev() for _ in range(4)] if times is not None else None
+        if e: e[0].record(s)
+        bsa.bsa_pool_qk(self.qd, self.kd, g, out=(self.qp, self.kp))
+        if e: e[1].record(s)
+        bsa.bsa_build_mask(self.qp, self.kp, g, self.p, out=(self.mask, self.cnt, self.idx, self.logw))
+        if e: e[2].record(s)
+        bsa.bsa_forward(self.qd, self.kd, self.vd, g, self.cnt, self.idx, self.logw, out=self.out,
+                        dense_split=self.split, workspace=self.ws)
+        if e:
+            e[3].record(s)
+            times.append(e)
+
+    def timed(self, steps):
+        """Whole steps bracketed by synchronize on both sides; per-stage HIP
+        events on the launch stream."""
+        import numpy as np
+        torch, w = self.torch, self.w
+        times = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        s0 = self.ev()
+        s0.record(self.stream)
+        for _ in range(steps):
+            self.step(times)
+        s1 = self.ev()
+        s1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = s0.elapsed_time(s1) / steps
+        pool_ms = float(np.median([e[0].elapsed_time(e[1]) for e in times]))
+        mask_ms = float(np.median([e[1].elapsed_time(e[2]) for e in times]))
+        fwd_times = [e[2].elapsed_time(e[3]) for e in times]
+        nqb, nkb, esz = self.nqb, self.nkb, (2 if w.dtype == "bf16" else 4)
+        pool_bytes = 2 * w.B * w.H * w.S * w.D * esz + w.B * w.H * (nqb + nkb) * w.D * 4
+        # mask: the logits are D non-fused multiplies and D adds each (the VALU-bound part); its bytes are
+        # the pooled summaries in, and the mask, counts, listed indices (and log-weights) out
+        mask_lane_ops = 2.0 * w.B * w.H * nqb * nkb * w.D
+        mask_bytes = (w.B * w.H * (nqb + nkb) * w.D * 4 + w.B * w.H * nqb * nkb + w.B * w.H * nqb * 4
+                      + self.blocks * 4 * (2 if self.logw is not None else 1))
+        return {"step_ms": step_ms, "wall": wall, "pool_ms": pool_ms, "mask_ms": mask_ms,
+                "fwd_ms": float(np.median(fwd_times)),          # ms per forward call: the median
+                "fwd_ms_mean": float(np.mean(fwd_times)),       # the average launch duration, for the roofline
+                "pool_bytes": pool_bytes, "mask_bytes": mask_bytes, "mask_lane_ops": mask_lane_ops}
+
+    def summary(self, m):
+        """Per-workload figures: forward, pooling and mask times and their roofline fractions."""
+        w = self.w
+        kernel = fwd_kernel_of(w)
+        tf = self.flops / (m["fwd_ms"] * 1e-3) / 1e12
+        tf_avg = self.flops / (m["fwd_ms_mean"] * 1e-3) / 1e12
+        pool_gbs = m["pool_bytes"] / (m["pool_ms"] * 1e-3) / 1e9
+        mask_tops = m["mask_lane_ops"] / (m["mask_ms"] * 1e-3) / 1e12
+        return {"B": w.B, "H": w.H, "head_dim": w.D, "seq_len": w.S, "q_block": w.q_block, "k_block": w.k_block,
+                "selection": w.mode, "keep_ratio": w.keep_ratio, "topk": w.topk, "dtype": w.dtype,
+                "text_columns": w.text_columns, "dense_split": self.split,
+                "ms_per_step": round(m["step_ms"], 4),
+                "step_tflops": round(self.flops / (m["step_ms"] * 1e-3) / 1e12, 2),
+                "fwd_kernel": kernel, "fwd_ms": round(m["fwd_ms"], 4), "fwd_ms_mean": round(m["fwd_ms_mean"], 4),
+                "fwd_tflops": round(tf, 2), "fwd_frac": round(tf_avg / PEAK_BF16_TFLOPS, 4),
+                "fwd_hbm_bytes": _profile_record("traffic", kernel, w.name, "hbm_bytes_per_launch"),
+                "pool_ms": round(m["pool_ms"], 4), "pool_gbs": round(pool_gbs, 1),
+                "pool_frac": round(pool_gbs / PEAK_HBM_GBS, 4),
+                "mask_ms": round(m["mask_ms"], 4), "mask_valu_frac": round(mask_tops / PEAK_VALU_TLANEOPS, 4),
+                "executed_blocks": self.blocks, "density": round(self.blocks / (w.B * w.H * self.nqb * self.nkb), 4)}
+
+
+HEADLINE = "wan_1p3b_keep10"
+OTHER_WORKLOADS = ("tiny_f32", "small_bf16", "wan_1p3b_sampled_k16", "hunyuan_keep08")
+
+
 def main():
     a = _args()
     if a.calibrate_copy_mib:
@@ -333,104 +465,25 @@ def main():
         print(f"bench.py runs on one GPU: the path has no multi-GPU part "
               f"(asked for --gpus {a.gpus})", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import block_sparse_attention_42_amd as bsa
     import workloads as W
 
     w = W.workload(a.workload)
-    t_gen = time.perf_counter()
-    q, k, v = W.generate(w)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    dev = torch.device("cuda:0")
-    qd, kd, vd = (torch.from_numpy(x).to(dt).to(dev) for x in (q, k, v))
-    if w.dtype == "bf16":     # what the oracle sees: the bf16 values
-        q, k, v = (t.float().cpu().numpy() for t in (qd, kd, vd))
-    t_gen = time.perf_counter() - t_gen
-    g = bsa.Geometry(w.B, w.H, w.text_len, w.frames, w.latent_h, w.latent_w, w.D, w.q_block, w.k_block,
-                     w.seq_alloc)
-    p = bsa.MaskParams(mode=w.mode, topk=w.topk, keep_ratio=w.keep_ratio, frame0_dense=w.frame0_dense,
-                       text_columns=w.text_columns, log_cluster=w.log_cluster, seed=w.sample_seed)
-    d = bsa.bsa_derive(g, p)
-    nqb, nkb = d["nqb"], d["nkb"]
-    qp = torch.empty((w.B, w.H, nqb, w.D), dtype=torch.float32, device=dev)
-    kp = torch.empty((w.B, w.H, nkb, w.D), dtype=torch.float32, device=dev)
-    mask = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.uint8, device=dev)
-    cnt = torch.empty((w.B, w.H, nqb), dtype=torch.int32, device=dev)
-    idx = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.int32, device=dev)
-    logw = torch.empty((w.B, w.H, nqb, nkb), dtype=torch.float32, device=dev) if w.mode == "sample" else None
-    out = torch.empty_like(qd)
-    stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-
-    split_box = [1, None]                 # dense_split, its workspace
-
-    def step(times=None):
-        e = [ev() for _ in range(4)] if times is not None else None
-        if e: e[0].record(stream)
-        bsa.bsa_pool_blocks(qd, g, g.q_block, out=qp)
-        bsa.bsa_pool_blocks(kd, g, g.k_block, out=kp)
-        if e: e[1].record(stream)
-        bsa.bsa_build_mask(qp, kp, g, p, out=(mask, cnt, idx, logw))
-        if e: e[2].record(stream)
-        bsa.bsa_forward(qd, kd, vd, g, cnt, idx, logw, out=out, dense_split=split_box[0], workspace=split_box[1])
-        if e:
-            e[3].record(stream)
-            times.append(e)
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    # the key split of the frame-0 rows: chosen from the lists, outside the timed region
-    split = bsa.suggest_dense_split(g, cnt) if a.dense_split == "auto" else int(a.dense_split)
-    if split != 1:
-        split_box[:] = [split, torch.empty(max(bsa.bsa_forward_split_workspace_bytes(g, split), 16),
-                                           dtype=torch.uint8, device=dev)]
-        for _ in range(2):
-            step()
-        torch.cuda.synchronize()
-    blocks = int(cnt.sum().item())
-    flops = 4.0 * w.D * w.q_block * w.k_block * blocks
-
-    # whole steps, bracketed by synchronize on both sides
-    times = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    s0 = ev()
-    s0.record(stream)
-    for _ in range(a.steps):
-        step(times)
-    s1 = ev()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = s0.elapsed_time(s1) / a.steps
-    pool_ms = float(np.median([e[0].elapsed_time(e[1]) for e in times]))
-    mask_ms = float(np.median([e[1].elapsed_time(e[2]) for e in times]))
-    fwd_times = [e[2].elapsed_time(e[3]) for e in times]
-    fwd_ms = float(np.median(fwd_times))           # ms per forward call: the median over the timed steps
-    fwd_ms_mean = float(np.mean(fwd_times))        # the average launch duration, for the roofline
-    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
-    fwd_tflops_avg = flops / (fwd_ms_mean * 1e-3) / 1e12
-    value = flops / (step_ms * 1e-3) / 1e12
-    pool_bytes = 2 * w.B * w.H * w.S * w.D * (2 if w.dtype == "bf16" else 4) + w.B * w.H * (nqb + nkb) * w.D * 4
-    # mask: the logits are D non-fused multiplies and D adds each (the VALU-bound part); its bytes are the
-    # pooled summaries in, and the mask, counts, listed indices (and log-weights) out
-    mask_lane_ops = 2.0 * w.B * w.H * nqb * nkb * w.D
-    mask_bytes = (w.B * w.H * (nqb + nkb) * w.D * 4 + w.B * w.H * nqb * nkb + w.B * w.H * nqb * 4
-                  + blocks * 4 * (2 if logw is not None else 1))
-
-    fwd_src = os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", "forward.hip")
-    traffic = _traffic(fwd_src, w.name)
-    mfma_busy = _mfma_busy(fwd_src, w.name)
+    run = PathRun(bsa, torch, w, a.warmup, a.dense_split, keep_host=not a.no_cpu_baseline)
+    m = run.timed(a.steps)
+    summ = run.summary(m)
+    kernel = summ["fwd_kernel"]
+    g, nqb, nkb = run.g, run.nqb, run.nkb
+    fwd_tflops_avg = run.flops / (m["fwd_ms_mean"] * 1e-3) / 1e12
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(run.flops / (m["step_ms"] * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": round(m["step_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -439,40 +492,58 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "head_dim": w.D, "seq_len": w.S,
                    "seq_alloc": w.seq_alloc, "q_block": w.q_block, "k_block": w.k_block,
                    "selection": w.mode, "keep_ratio": w.keep_ratio, "frame0_dense": w.frame0_dense,
-                   "text_columns": w.text_columns, "dense_split": split_box[0]},
-        "fwd_ms_per_call": round(fwd_ms, 4),
-        "fwd_ms_mean": round(fwd_ms_mean, 4),
-        "fwd_tflops": round(fwd_tflops, 2),
-        "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-        "pool_ms": round(pool_ms, 4),
-        "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
-        "pool_hbm": {"bound": "hbm", "achieved": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "mask_ms": round(mask_ms, 4),
-        "mask_gbs": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
-        "mask_valu": {"bound": "alu", "achieved": round(mask_lane_ops / (mask_ms * 1e-3) / 1e12, 2),
+                   "text_columns": w.text_columns, "dense_split": run.split},
+        "fwd_ms_per_call": summ["fwd_ms"],
+        "fwd_ms_mean": summ["fwd_ms_mean"],
+        "fwd_tflops": summ["fwd_tflops"],
+        "fwd_frac_of_bf16_peak": round(summ["fwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "pool_ms": summ["pool_ms"],
+        "pool_gbs": summ["pool_gbs"],
+        "pool_hbm": {"bound": "hbm", "achieved": summ["pool_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": summ["pool_frac"]},
+        "mask_ms": summ["mask_ms"],
+        "mask_gbs": round(m["mask_bytes"] / (m["mask_ms"] * 1e-3) / 1e9, 1),
+        "mask_valu": {"bound": "alu",
+                      "achieved": round(m["mask_lane_ops"] / (m["mask_ms"] * 1e-3) / 1e12, 2),
                       "peak": round(PEAK_VALU_TLANEOPS, 2), "unit": "T lane-ops/s",
-                      "frac": round(mask_lane_ops / (mask_ms * 1e-3) / 1e12 / PEAK_VALU_TLANEOPS, 4)},
-        "executed_blocks": blocks,
-        "density": round(blocks / (w.B * w.H * nqb * nkb), 4),
-        "wall_s_timed": round(wall, 3),
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(fwd_tflops_avg, 2),
+                      "frac": summ["mask_valu_frac"]},
+        "executed_blocks": run.blocks,
+        "density": summ["density"],
+        "wall_s_timed": round(m["wall"], 3),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(fwd_tflops_avg, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tflops_avg / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "mfma_busy": mfma_busy},
+                     "frac": round(fwd_tflops_avg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _profile_record("traffic", kernel, w.name, "hbm_bytes_per_launch"),
+                     "mfma_busy": _profile_record("sq", kernel, w.name, "mfma_busy_frac"),
+                     "clock_ghz": _profile_record("sq", kernel, w.name, "clock_ghz")},
     }
+    qd, kd, vd, kp, stream, ev = run.qd, run.kd, run.vd, run.kp, run.stream, run.ev
     if not a.no_graph:
-        res["graph_step"] = graph_timing(torch, step, stream, ev, a.steps, out)
+        res["graph_step"] = graph_timing(torch, run.step, stream, ev, a.steps, run.out)
     if a.cluster_clusters > 0 and a.cluster_clusters * nkb <= 16384:
-        res["cluster_selector"] = cluster_selector_timing(bsa, w, g, p, qd, kp, a.cluster_clusters,
+        res["cluster_selector"] = cluster_selector_timing(bsa, w, g, run.p, qd, kp, a.cluster_clusters,
                                                           a.cluster_iters, nqb, nkb, stream, ev)
     if not a.no_top_p and nkb <= 2048:
         res["top_p_selector"] = top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev)
     if not a.no_structured:
         res["structured_lists"] = structured_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev)
     if not a.no_cpu_baseline:
+        q, k, v = run.host
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_sample_qblocks, a.cpu_sample_heads)
-    res["input_gen_s"] = round(t_gen, 1)
+        del run.host, q, k, v
+    res["input_gen_s"] = round(run.input_gen_s, 1)
+    del run, qd, kd, vd, kp
+    torch.cuda.empty_cache()
+    # the other workloads: the same step, fewer steps, figures only
+    names = [] if a.configs == "none" else (
+        [n for n in OTHER_WORKLOADS if n != w.name] if a.configs == "all" else a.configs.split(","))
+    if names:
+        res["configs"] = {w.name: summ}
+        for name in names:
+            r = PathRun(bsa, torch, W.workload(name), a.config_warmup)
+            res["configs"][name] = r.summary(r.timed(a.config_steps))
+            del r
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

@@ -9,8 +9,7 @@ PyTorch fallback.
 
     g = Geometry(B, H, text_len, frames, latent_h, latent_w, head_dim,
                  q_block, k_block, seq_alloc)
-    qp = bsa_pool_blocks(q, g, g.q_block)
-    kp = bsa_pool_blocks(k, g, g.k_block)
+    qp, kp = bsa_pool_qk(q, k, g)      # or bsa_pool_blocks(q, g, g.q_block), ...(k, g, g.k_block)
     mask, cnt, idx, logw = bsa_build_mask(qp, kp, g, MaskParams(keep_ratio=0.1))
     out, lse = bsa_forward(q, k, v, g, cnt, idx, logw)
 
@@ -31,7 +30,7 @@ import torch
 from . import _lib
 from ._lib import BsaError
 
-__all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks",
+__all__ = ["Geometry", "MaskParams", "BsaError", "bsa_derive", "bsa_pool_blocks", "bsa_pool_qk",
            "bsa_build_mask", "bsa_forward", "bsa_forward_ex", "bsa_cluster_importance", "bsa_select_blocks",
            "bsa_select_top_p", "DOMAINS", "HEAD_CLASSES", "LAUNCH_ORDERS", "bsa_frame_scores", "bsa_classify_heads",
            "bsa_structured_lists", "library_path"]
@@ -131,6 +130,22 @@ def bsa_pool_blocks(x: torch.Tensor, g: Geometry, block: int, out: Optional[torc
     _lib.check(_lib.lib().bsa_pool_blocks(_ptr(x), _dtype_code(x), ctypes.byref(g.c()), block,
                                           _ptr(out), _stream(stream)))
     return out
+
+
+def bsa_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geometry, out=None, stream=None):
+    """bsa_pool_blocks of q with q_block and of k with k_block in one launch -> (q_pooled, k_pooled)."""
+    d = bsa_derive(g)
+    _need(q, "q", (g.B, g.H, g.seq_alloc, g.head_dim))
+    _need(k, "k", (g.B, g.H, g.seq_alloc, g.head_dim), q.dtype, q.device)
+    if out is None:
+        out = (torch.empty((g.B, g.H, d["nqb"], g.head_dim), dtype=torch.float32, device=q.device),
+               torch.empty((g.B, g.H, d["nkb"], g.head_dim), dtype=torch.float32, device=q.device))
+    qp, kp = out
+    _need(qp, "q_pooled", (g.B, g.H, d["nqb"], g.head_dim), torch.float32, q.device)
+    _need(kp, "k_pooled", (g.B, g.H, d["nkb"], g.head_dim), torch.float32, q.device)
+    _lib.check(_lib.lib().bsa_pool_qk(_ptr(q), _ptr(k), _dtype_code(q), ctypes.byref(g.c()), _ptr(qp), _ptr(kp),
+                                      _stream(stream)))
+    return qp, kp
 
 
 def bsa_build_mask(q_pooled: torch.Tensor, k_pooled: torch.Tensor, g: Geometry, p: MaskParams,

@@ -15,7 +15,7 @@ BSA_SELECT_TOPK = 0
 BSA_SELECT_SAMPLE = 1
 BSA_SPLIT_STATIC_MAX_BYTES = 33554432
 
-EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
+EXPORTED = ["bsa_derive", "bsa_pool_blocks", "bsa_pool_qk", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
             "bsa_forward_split", "bsa_forward_split_workspace_bytes", "bsa_forward_split_static",
             "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes", "bsa_select_top_p",
             "bsa_frame_scores", "bsa_classify_heads", "bsa_structured_lists",
@@ -78,6 +78,7 @@ def lib():
         M = ctypes.POINTER(bsa_mask_params)
         L.bsa_derive.argtypes = [G, M, ctypes.POINTER(bsa_derived)]
         L.bsa_pool_blocks.argtypes = [P, ctypes.c_int32, G, ctypes.c_int32, P, P]
+        L.bsa_pool_qk.argtypes = [P, P, ctypes.c_int32, G, P, P, P]
         L.bsa_build_mask.argtypes = [P, P, G, M, P, P, P, P, P]
         L.bsa_forward.argtypes = [P, P, P, ctypes.c_int32, G, P, P, P, ctypes.c_float, P, P, P]
         L.bsa_forward_ex.argtypes = [P, P, P, ctypes.c_int32, G, P, P, P, ctypes.c_float, P, P,
@@ -96,7 +97,7 @@ def lib():
         L.bsa_frame_scores.argtypes = [P, G, ctypes.c_int32, P, P]
         L.bsa_classify_heads.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
         L.bsa_structured_lists.argtypes = [P, G, ctypes.POINTER(bsa_struct_params), P, P, P, P]
-        for f in ("bsa_derive", "bsa_pool_blocks", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
+        for f in ("bsa_derive", "bsa_pool_blocks", "bsa_pool_qk", "bsa_build_mask", "bsa_forward", "bsa_forward_ex",
                   "bsa_forward_split", "bsa_forward_split_workspace_bytes", "bsa_forward_split_static",
                   "bsa_abi_version",
                   "bsa_cluster_importance", "bsa_select_blocks", "bsa_top_p_workspace_bytes",

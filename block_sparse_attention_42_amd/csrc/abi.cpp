@@ -168,6 +168,36 @@ bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, 
   return ok();
 }
 
+bsa_status bsa_pool_qk(const void* q, const void* k, int32_t dtype, const bsa_geometry* g, float* q_pooled,
+                       float* k_pooled, void* stream) {
+  Derived d;
+  bsa_status s = check_geometry(g, &d);
+  if (s != BSA_OK) return s;
+  if (dtype != BSA_DTYPE_BF16 && dtype != BSA_DTYPE_F32)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (!q || !k || !q_pooled || !k_pooled)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, q_pooled and k_pooled must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_pooled) || !aligned16(k_pooled))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, q_pooled and k_pooled must be 16-byte aligned");
+  bsa::PoolArgs a[2];
+  const void* x[2] = {q, k};
+  float* out[2] = {q_pooled, k_pooled};
+  const int32_t block[2] = {g->q_block, g->k_block};
+  for (int j = 0; j < 2; ++j) {
+    a[j].x = x[j];
+    a[j].out = out[j];
+    a[j].seq_alloc = g->seq_alloc;
+    a[j].S = d.S;
+    a[j].BH = g->B * g->H;
+    a[j].D = g->head_dim;
+    a[j].block = block[j];
+    a[j].nb = (int32_t)((d.S + block[j] - 1) / block[j]);
+  }
+  hipError_t e = bsa::launch_pool_jobs(a, 2, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BSA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bsa_geometry* g,
                           const bsa_mask_params* p, uint8_t* mask, int32_t* kv_cnt,
                           int32_t* kv_idx, float* log_w, void* stream) {
@@ -198,8 +228,6 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
   a.nqb = d.nqb;
   a.nkb = d.nkb;
   a.D = g->head_dim;
-  int rows = 32768 / d.nkb;
-  a.rows_per_group = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
   a.mode = p->mode;
   a.topk = topk_of(p, d.nkb);
   a.expected = (float)(p->keep_ratio * (double)d.nkb);
@@ -293,8 +321,6 @@ bsa_status bsa_select_blocks(const float* importance, const bsa_geometry* g, con
   a.nqb = d.nqb;
   a.nkb = d.nkb;
   a.D = g->head_dim;
-  int rows = 32768 / d.nkb;
-  a.rows_per_group = rows < 1 ? 1 : (rows > 16 ? 16 : rows);
   a.mode = p->mode;
   a.topk = topk_of(p, d.nkb);
   a.expected = (float)(p->keep_ratio * (double)d.nkb);

@@ -30,7 +30,6 @@ struct MaskArgs {
   int32_t* idx;       // [BH, nqb, nkb]
   float* logw;        // [BH, nqb, nkb] or null
   int32_t H, BH, nqb, nkb, D;
-  int32_t rows_per_group;
   int32_t mode;       // 0 top-k, 1 sample
   int32_t topk;
   float expected;
@@ -153,6 +152,8 @@ constexpr int64_t kStaticScratchBytes = 32LL << 20;
 hipError_t static_scratch(float** ptr);
 
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t stream);
+// Pools one or two tensors (jobs[0], jobs[1]) in a single launch.
+hipError_t launch_pool_jobs(const PoolArgs* jobs, int njobs, int dtype, hipStream_t stream);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream);
 int importance_group(int C, int nkb, int nqb);
 size_t importance_lds_bytes(const ImpArgs& a);

@@ -7,7 +7,11 @@
 // one-key-per-row safeguard); "AB-Attention" (TL;DR: blocks sampled in
 // proportion to importance, reweighted by inverse inclusion probability).
 //
-// One workgroup (8 waves) takes R consecutive query blocks of one head:
+// One workgroup (8 waves) takes R consecutive query blocks of one head (R
+// is 8 or 4, chosen per launch so that the grid holds at least three
+// workgroups per CU; at most 128 registers a lane and at most half a CU's
+// LDS let two workgroups share a CU, so that one's selection overlaps the
+// other's logits):
 //   A. all 512 threads compute the R x nkb float32 logits into LDS, each
 //      logit as a sequential non-fused multiply-add chain over D in
 //      ascending order (the library's contract, so the integer decisions
@@ -20,6 +24,8 @@
 //      sampling, exp / water-filling / Philox draws (one evaluation per four
 //      blocks) / log-weights.  Frame-0 rows skip straight to "all blocks";
 //      text columns are OR-ed in.
+#include <atomic>
+
 #include "bsa_internal.h"
 #include "spec_math.h"
 
@@ -28,9 +34,9 @@ namespace {
 
 constexpr int kMaskThreads = 512;
 constexpr int kMaskWaves = kMaskThreads / 64;
-constexpr int kMaxRows = 16;
-constexpr int kZFloats = 32768;          // LDS logits budget: rows * nkb <= 32768
 constexpr int kMaxPerLane = 32;          // sampling: nkb <= 64 * 32
+constexpr int kRegKeys = 64 * kMaxPerLane;   // top-k rows up to this length keep their keys in registers
+constexpr size_t kMaskLdsCap = 160 * 1024;
 
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -170,26 +176,102 @@ __device__ __forceinline__ void topk_row(const float* zr, int n, int k, int text
   if (lane == 0) *cnt_out = run_sel;
 }
 
-// JT: key blocks per thread in the logits phase (1, 2 or 4).
-template <int JT>
-__global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
-  // k chunks loaded together: a 64-byte run of each key row when JT = 4
-  // (measured 8-10 % faster there; with JT = 1 it is slower)
-  constexpr int KB = JT == 4 ? 4 : 1;
-  __shared__ float zs[kZFloats];
-  __shared__ float qs[kMaxRows * 128];
-  __shared__ int hist_all[kMaskWaves * 256];
+// Logits of R query rows (q rows in LDS) against every key block: thread tid
+// owns key blocks base + tid + jj * kMaskThreads for each pass `base`.  Each
+// logit is the sequential non-fused chain over d ascending.  A thread's key
+// row is read in 16-byte chunks kept PF chunks ahead of their use (one
+// 128-byte line per key in flight when JT = 1).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int R, int JT, int D>
+__device__ __forceinline__ void logits_rows(const MaskArgs& a, const float* kbase, const float* q, float* zs,
+                                            int n, int nrows, int tid) {
+  constexpr int NC = D / 4;
+  constexpr int PF = 8 / JT;
+  for (int base = 0; base < n; base += kMaskThreads * JT) {
+    float acc[R][JT];
+    const f32x4_t* kr[JT];
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = min(base + tid + jj * kMaskThreads, n - 1);
+      kr[jj] = reinterpret_cast<const f32x4_t*>(kbase + (int64_t)j * D);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][jj] = 0.0f;
+    }
+    f32x4_t ring[PF][JT];
+#pragma unroll
+    for (int c = 0; c < PF; ++c)
+#pragma unroll
+      for (int jj = 0; jj < JT; ++jj) ring[c][jj] = kr[jj][c];
+#pragma nounroll
+    for (int c0 = 0; c0 < NC; c0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int c = c0 + u;
+        f32x4_t kv[JT];
+#pragma unroll
+        for (int jj = 0; jj < JT; ++jj) {
+          kv[jj] = ring[u][jj];
+          ring[u][jj] = kr[jj][min(c + PF, NC - 1)];   // past the row's end: a harmless reread
+        }
+        f32x4_t qc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) qc[r] = *reinterpret_cast<const f32x4_t*>(q + r * D + 4 * c);
+        // the R x JT chains advance together, one component at a time
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int jj = 0; jj < JT; ++jj) acc[r][jj] = __fadd_rn(acc[r][jj], __fmul_rn(qc[r][e], kv[jj][e]));
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = base + tid + jj * kMaskThreads;
+      if (j < n) {
+        const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r < nrows) {
+            float z = __fmul_rn(acc[r][jj], a.scale);
+            if (a.log_cluster) z = __fadd_rn(z, lc);
+            if (z == 0.0f) z = 0.0f;                // -0 -> +0
+            zs[r * n + j] = z;
+          }
+        }
+      }
+    }
+  }
+}
+
+// LDS of one workgroup: the R x nkb logits, the R query rows and (top-k rows
+// longer than kRegKeys only) one 256-bin histogram per wave.
+__host__ __device__ constexpr size_t mask_lds_bytes(int R, int n, int D, bool radix) {
+  return ((size_t)R * n + (size_t)R * D) * 4 + (radix ? (size_t)kMaskWaves * 256 * 4 : 0);
+}
+
+// R: query blocks per workgroup; JT: key blocks per thread in the logits
+// phase (1 or 2); SAMPLE: the selection mode (a kernel per mode keeps the
+// top-k kernel's registers free of the sampling state).
+template <int R, int JT, bool SAMPLE>
+__global__ __launch_bounds__(kMaskThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void mask_kernel(MaskArgs a) {
+  constexpr int kMaxRows = R;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int R = a.rows_per_group;
   const int ngroups = (a.nqb + R - 1) / R;
   const int bh = blockIdx.x / ngroups;
   const int i0 = (blockIdx.x % ngroups) * R;
   const int nrows = min(R, a.nqb - i0);
   const int n = a.nkb;
   const int D = a.D;
+  float* zs = lds;                                           // [R][n]
+  float* qs = lds + (size_t)R * n;                           // [R][D]
+  int* hist_all = reinterpret_cast<int*>(qs + (size_t)R * (a.imp ? 0 : D));   // [waves][256]
 
   // ---- A. logits (or the given importance rows) ---------------------------
   // Each thread owns all R rows x JT key blocks: every wave reads the same q
@@ -204,59 +286,9 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
     const float* qsrc = a.qp + ((int64_t)bh * a.nqb + i0) * D;
     for (int e = tid; e < kMaxRows * D; e += kMaskThreads) qs[e] = e < nrows * D ? qsrc[e] : 0.0f;
     __syncthreads();
-    {
-      const float* kbase = a.kp + (int64_t)bh * n * D;
-      for (int base = 0; base < n; base += kMaskThreads * JT) {
-        float acc[kMaxRows][JT];
-        const float* kr[JT];
-#pragma unroll
-        for (int jj = 0; jj < JT; ++jj) {
-          const int j = min(base + tid + jj * kMaskThreads, n - 1);
-          kr[jj] = kbase + (int64_t)j * D;
-#pragma unroll
-          for (int r = 0; r < kMaxRows; ++r) acc[r][jj] = 0.0f;
-        }
-        for (int d0 = 0; d0 < D; d0 += 4 * KB) {
-          float4 kv[KB][JT];
-#pragma unroll
-          for (int b = 0; b < KB; ++b)
-#pragma unroll
-            for (int jj = 0; jj < JT; ++jj) kv[b][jj] = *reinterpret_cast<const float4*>(kr[jj] + d0 + 4 * b);
-#pragma unroll
-          for (int b = 0; b < KB; ++b) {
-#pragma unroll
-            for (int r = 0; r < kMaxRows; ++r) {
-              const float4 qv = *reinterpret_cast<const float4*>(qs + r * D + d0 + 4 * b);
-#pragma unroll
-              for (int jj = 0; jj < JT; ++jj) {
-                float t = acc[r][jj];
-                t = __fadd_rn(t, __fmul_rn(qv.x, kv[b][jj].x));
-                t = __fadd_rn(t, __fmul_rn(qv.y, kv[b][jj].y));
-                t = __fadd_rn(t, __fmul_rn(qv.z, kv[b][jj].z));
-                t = __fadd_rn(t, __fmul_rn(qv.w, kv[b][jj].w));
-                acc[r][jj] = t;
-              }
-            }
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < JT; ++jj) {
-          const int j = base + tid + jj * kMaskThreads;
-          if (j < n) {
-            const float lc = (j == n - 1) ? a.ln_last : a.ln_full;
-#pragma unroll
-            for (int r = 0; r < kMaxRows; ++r) {
-              if (r < nrows) {
-                float z = __fmul_rn(acc[r][jj], a.scale);
-                if (a.log_cluster) z = __fadd_rn(z, lc);
-                if (z == 0.0f) z = 0.0f;                // -0 -> +0
-                zs[r * n + j] = z;
-              }
-            }
-          }
-        }
-      }
-    }
+    const float* kbase = a.kp + (int64_t)bh * n * D;
+    if (D == 128) logits_rows<R, JT, 128>(a, kbase, qs, zs, n, nrows, tid);
+    else logits_rows<R, JT, 64>(a, kbase, qs, zs, n, nrows, tid);
   }
   __syncthreads();
 
@@ -281,7 +313,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
     }
     const float* zr = zs + r * n;
 
-    if (a.mode == 0 && n <= 64 * kMaxPerLane) {
+    if (!SAMPLE && n <= kRegKeys) {
       int P = 64;
       while (P < n) P <<= 1;
       int32_t* co = a.cnt + rowid;
@@ -295,7 +327,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
       }
       continue;
     }
-    if (a.mode == 0) {
+    if (!SAMPLE) {
       // rows longer than the register budget: radix select over LDS
       uint32_t T;
       int need;
@@ -398,24 +430,24 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
         if (4 * cc + w < n) ur[4 * cc + w] = (float)(uint32_t)(x[w] >> 40);
     }
     wave_lds_sync();
-    // pi, draws
-    uint32_t selbits = 0;
-    float pi[kMaxPerLane];
+    // pi_j = 1 for capped blocks (and all of a row with E >= n), else c e_j;
+    // recomputed where needed rather than held, to keep registers free
+    auto pi_of = [&](int mm) { return (all_in || ((cap >> mm) & 1u)) ? 1.0f : __fmul_rn(c, e[mm]); };
+    // draws
+    uint32_t selbits = 0, forced = 0;
 #pragma unroll
     for (int mm = 0; mm < kMaxPerLane; ++mm) {
       const int j = lane + 64 * mm;
-      pi[mm] = (all_in || ((cap >> mm) & 1u)) ? 1.0f : __fmul_rn(c, e[mm]);
       if (mm < per && j < n) {
         const float u = ur[j] * 5.9604644775390625e-08f;   // 2^-24
-        if (u < pi[mm]) selbits |= 1u << mm;
+        if (u < pi_of(mm)) selbits |= 1u << mm;
       }
     }
     const bool any_sel = __any(selbits != 0);
     if (!any_sel && (am & 63) == lane) {
       // safeguard block: kept with weight 0
-#pragma unroll
-      for (int mm = 0; mm < kMaxPerLane; ++mm)
-        if (mm == (am >> 6)) { selbits |= 1u << mm; pi[mm] = 1.0f; }
+      selbits |= 1u << (am >> 6);
+      forced = 1u << (am >> 6);
     }
     int run_sel = 0;
 #pragma unroll
@@ -424,7 +456,8 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
         const int j = lane + 64 * mm;
         const bool in = j < n;
         bool sel = in && ((selbits >> mm) & 1u);
-        float w = (sel && pi[mm] < 1.0f) ? -logf(pi[mm]) : 0.0f;
+        const float pim = ((forced >> mm) & 1u) ? 1.0f : pi_of(mm);
+        float w = (sel && pim < 1.0f) ? -logf(pim) : 0.0f;
         if (in && j <= a.text_last) { sel = true; w = 0.0f; }
         const uint64_t bsel = __ballot(sel);
         const int pos = run_sel + __popcll(bsel & below);
@@ -442,23 +475,66 @@ __global__ __launch_bounds__(kMaskThreads) void mask_kernel(MaskArgs a) {
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_mask_lds_raised[kMaxDevices];   // per device: bit per (R, JT)
+
+template <int R, int JT, bool SAMPLE>
+hipError_t launch_rj(const MaskArgs& a, size_t lds, unsigned grid, hipStream_t stream) {
+  const void* f = reinterpret_cast<const void*>(&mask_kernel<R, JT, SAMPLE>);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = 1u << (4 * (SAMPLE ? 1 : 0) + 2 * (R == 8 ? 1 : 0) + (JT == 1 ? 0 : 1));
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (lds > 64 * 1024 && (!known || !(g_mask_lds_raised[dev].load(std::memory_order_acquire) & bit))) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaskLdsCap);
+    if (e != hipSuccess) return e;
+    if (known) g_mask_lds_raised[dev].fetch_or(bit, std::memory_order_release);
+  }
+  hipLaunchKernelGGL((mask_kernel<R, JT, SAMPLE>), dim3(grid), dim3(kMaskThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int R, bool SAMPLE>
+hipError_t launch_rs(const MaskArgs& a, int jt, size_t lds, unsigned grid, hipStream_t stream) {
+  if (jt == 2) return launch_rj<R, 2, SAMPLE>(a, lds, grid, stream);
+  return launch_rj<R, 1, SAMPLE>(a, lds, grid, stream);
+}
+
+template <int R>
+hipError_t launch_r(const MaskArgs& a, int jt, size_t lds, unsigned grid, hipStream_t stream) {
+  return a.mode == 1 ? launch_rs<R, true>(a, jt, lds, grid, stream) : launch_rs<R, false>(a, jt, lds, grid, stream);
+}
+
+}  // namespace
+
 hipError_t launch_mask(const MaskArgs& a, hipStream_t stream) {
-  const int ngroups = (a.nqb + a.rows_per_group - 1) / a.rows_per_group;
+  const bool radix = a.mode == 0 && a.nkb > kRegKeys;
+  const int D = a.imp ? 0 : a.D;
+  // rows per workgroup: eight (each key-row read feeds R logits) if the grid
+  // still holds three workgroups per CU and two fit a CU's LDS; else four
+  int R = 4;
+  for (int r : {8}) {
+    const int64_t groups = (int64_t)a.BH * ((a.nqb + r - 1) / r);
+    if (groups >= 3 * 256 && mask_lds_bytes(r, a.nkb, D, radix) <= kMaskLdsCap / 2) { R = r; break; }
+  }
+  const size_t lds = mask_lds_bytes(R, a.nkb, D, radix);
+  if (lds > kMaskLdsCap) return hipErrorInvalidValue;
+  const int ngroups = (a.nqb + R - 1) / R;
   const int64_t grid = (int64_t)a.BH * ngroups;
   // key blocks per thread: the fewest passes x JT (per-lane work), ties to
   // the larger JT (fewer q reads per product).  Splitting a workgroup's rows
   // over thread groups (fewer rows, more key blocks per thread) measured
   // slower at every shape tried: it multiplies the scattered k reads.
   int jt = 1, best = 1 << 30;
-  for (int t : {1, 2, 4}) {
+  for (int t : {1, 2}) {
     const int work = ((a.nkb + kMaskThreads * t - 1) / (kMaskThreads * t)) * t;
     if (work <= best) { best = work; jt = t; }
   }
-  const dim3 g((unsigned)grid), b(kMaskThreads);
-  if (jt == 4) hipLaunchKernelGGL(mask_kernel<4>, g, b, 0, stream, a);
-  else if (jt == 2) hipLaunchKernelGGL(mask_kernel<2>, g, b, 0, stream, a);
-  else hipLaunchKernelGGL(mask_kernel<1>, g, b, 0, stream, a);
-  return hipGetLastError();
+  if (R == 8) return launch_r<8>(a, jt, lds, (unsigned)grid, stream);
+  return launch_r<4>(a, jt, lds, (unsigned)grid, stream);
 }
 
 }  // namespace bsa

@@ -157,6 +157,18 @@ bsa_status bsa_derive(const bsa_geometry* g, const bsa_mask_params* p, bsa_deriv
 bsa_status bsa_pool_blocks(const void* x, int32_t dtype, const bsa_geometry* g, int32_t block,
                            float* pooled, void* stream);
 
+/* Pooling of Q and K in one launch: q_pooled as bsa_pool_blocks(q, ...,
+ * q_block) and k_pooled as bsa_pool_blocks(k, ..., k_block) compute them,
+ * bit for bit (same definition, same pages).  One launch instead of two
+ * saves a launch and a drain between them.
+ *   q, k:     [B, H, seq_alloc, D] of `dtype`.
+ *   q_pooled: [B, H, nqb, D] float32, written.
+ *   k_pooled: [B, H, nkb, D] float32, written.
+ *   Errors: an unknown dtype, NULL or misaligned buffers
+ *   (BSA_ERR_INVALID_ARGUMENT, before any launch). */
+bsa_status bsa_pool_qk(const void* q, const void* k, int32_t dtype, const bsa_geometry* g, float* q_pooled,
+                       float* k_pooled, void* stream);
+
 /* Block logits, selection, overrides and compaction (frame-0 page secs. 4,
  * 6, 7; EG-Sparse page Eq. 2 and the one-key safeguard; AB-Attention page
  * sampling and reweighting).

@@ -105,6 +105,12 @@ int main(void) {
   EXPECT(bsa_pool_blocks(fake, 7, &small, 64, fake, NULL) == BSA_ERR_INVALID_ARGUMENT);
   EXPECT(bsa_pool_blocks(fake, 0, &small, 48, fake, NULL) == BSA_ERR_INVALID_ARGUMENT);
 
+  EXPECT(bsa_pool_qk(fake, fake, 0, &small, fake, NULL, NULL) == BSA_ERR_INVALID_ARGUMENT);
+  EXPECT(bsa_pool_qk(fake, mis, 0, &small, fake, fake, NULL) == BSA_ERR_INVALID_ARGUMENT);
+  EXPECT(bsa_pool_qk(fake, fake, 2, &small, fake, fake, NULL) == BSA_ERR_INVALID_ARGUMENT);
+  EXPECT(bsa_pool_qk(fake, fake, 0, NULL, fake, fake, NULL) == BSA_ERR_INVALID_ARGUMENT);
+  EXPECT(bsa_pool_qk(fake, fake, 0, &huge, fake, fake, NULL) == BSA_ERR_UNSUPPORTED);
+
   /* mask */
   EXPECT(bsa_build_mask(NULL, fake, &small, &p, NULL, fake, fake, NULL, NULL) == BSA_ERR_INVALID_ARGUMENT);
   EXPECT(bsa_build_mask(fake, fake, &small, NULL, NULL, fake, fake, NULL, NULL) == BSA_ERR_INVALID_ARGUMENT);

@@ -78,6 +78,9 @@ def test_validation_rejects_before_launch():
     assert L.bsa_pool_blocks(mis, 0, ctypes.byref(g), 64, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert L.bsa_pool_blocks(fake, 7, ctypes.byref(g), 64, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
     assert L.bsa_pool_blocks(fake, 0, ctypes.byref(g), 48, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_pool_qk(fake, None, 0, ctypes.byref(g), fake, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_pool_qk(fake, fake, 0, ctypes.byref(g), mis, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
+    assert L.bsa_pool_qk(fake, fake, 3, ctypes.byref(g), fake, fake, None) == _lib.BSA_ERR_INVALID_ARGUMENT
     bad = _geo(w.replace(D=96)).c()
     assert L.bsa_pool_blocks(fake, 0, ctypes.byref(bad), 64, fake, None) == _lib.BSA_ERR_UNSUPPORTED
     bad = _geo(w.replace(q_block=128, align=128)).c()

@@ -59,8 +59,10 @@ def run_gpu(w, q, k, v, want_lse=True):
     _say(f"[gpu] {w.name} B={w.B} H={w.H} S={w.S} D={w.D} bq={w.q_block} bk={w.k_block} mode={w.mode}")
     g = _geo(w)
     qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
-    qp = bsa.bsa_pool_blocks(qd, g, g.q_block)
-    kp = bsa.bsa_pool_blocks(kd, g, g.k_block)
+    qp, kp = bsa.bsa_pool_qk(qd, kd, g)          # one launch, as bench.py pools
+    # the one-tensor entry point computes the same means, bit for bit
+    assert torch.equal(bsa.bsa_pool_blocks(qd, g, g.q_block).view(torch.int32), qp.view(torch.int32))
+    assert torch.equal(bsa.bsa_pool_blocks(kd, g, g.k_block).view(torch.int32), kp.view(torch.int32))
     mask, cnt, idx, logw = bsa.bsa_build_mask(qp, kp, g, _mp(w))
     # NaN-filled outputs: every row (valid or pad) must be written by the kernel
     out = torch.full_like(qd, float("nan"))
