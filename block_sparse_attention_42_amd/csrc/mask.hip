@@ -57,6 +57,19 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011) -------------------
+// 128-bit product of two 64-bit words from four 32 x 32 -> 64 multiply-adds:
+// with a = a1 2^32 + a0 and b likewise, t = a1 b0 + hi(a0 b0) and
+// u = a0 b1 + lo(t) cannot overflow, and a b = (a1 b1 + hi(t) + hi(u)) 2^64
+// + lo(u) 2^32 + lo(a0 b0).
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32), b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t t = (uint64_t)a1 * b0 + (p00 >> 32);
+  const uint64_t u = (uint64_t)a0 * b1 + (uint32_t)t;
+  lo = (u << 32) | (uint32_t)p00;
+  hi = (uint64_t)a1 * b1 + (t >> 32) + (u >> 32);
+}
+
 // The four 64-bit output words of counter (c0, c1, 0, 0) under key (k0, 0).
 __device__ __forceinline__ void philox4(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t (&x)[4]) {
   const uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
@@ -66,8 +79,9 @@ __device__ __forceinline__ void philox4(uint64_t c0, uint64_t c1, uint64_t k0, u
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r > 0) { key0 += kW0; key1 += kW1; }
-    const uint64_t hi0 = __umul64hi(kM0, x0), lo0 = kM0 * x0;
-    const uint64_t hi1 = __umul64hi(kM1, x2), lo1 = kM1 * x2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(kM0, x0, hi0, lo0);
+    mulhilo64(kM1, x2, hi1, lo1);
     const uint64_t n0 = hi1 ^ x1 ^ key0, n2 = hi0 ^ x3 ^ key1;
     x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
   }
