@@ -167,5 +167,7 @@ hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t
 // picks it for them).
 bool forward_wide_supported(int dtype, int head_dim, int q_block, int k_block);
 hipError_t launch_forward_wide(const FwdArgs& a, hipStream_t stream);
+// The float32 forward (float32 matrix products and softmax).
+hipError_t launch_forward_f32(const FwdArgs& a, int head_dim, hipStream_t stream);
 
 }  // namespace bsa

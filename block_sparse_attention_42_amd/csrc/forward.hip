@@ -46,7 +46,9 @@ using namespace fwdc;
 template <typename T, int D, int QT, int BK>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64), amdgpu_waves_per_eu(1, 1)))
 void fwd_kernel(FwdArgs a) {
-  constexpr bool kDma = sizeof(T) == 2;  // bf16 tiles go HBM -> LDS directly; f32 is converted in registers
+  // bf16 tiles go HBM -> LDS directly (the kernel is instantiated for bf16
+  // only: float32 inputs take the float32 kernel)
+  constexpr bool kDma = sizeof(T) == 2;
   constexpr uint32_t ES = sizeof(T);
   constexpr uint32_t RB = D * ES;      // bytes per K/V row in memory
   constexpr int KC = D / 16;           // k chunks of the Q.K contraction (32x32x16)
@@ -898,9 +900,10 @@ hipError_t launch_d(const FwdArgs& a, int head_dim, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, int head_dim, hipStream_t stream) {
-  const hipError_t e = forward_wide_supported(dtype, head_dim, a.q_block, a.k_block)
+  const hipError_t e = dtype != 0 ? launch_forward_f32(a, head_dim, stream)
+                       : forward_wide_supported(dtype, head_dim, a.q_block, a.k_block)
                            ? launch_forward_wide(a, stream)
-                           : (dtype == 0 ? launch_d<bf16_t>(a, head_dim, stream) : launch_d<float>(a, head_dim, stream));
+                           : launch_d<bf16_t>(a, head_dim, stream);
   if (e != hipSuccess || a.split <= 1 || a.n_dense == 0) return e;
   return dtype == 0 ? launch_merge<bf16_t>(a, head_dim, stream) : launch_merge<float>(a, head_dim, stream);
 }

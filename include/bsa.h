@@ -194,8 +194,7 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
 
 /* Exact attention on the selected blocks (AB-Attention page, TL;DR and
  * "Gather kernel"/"Reweighted attention" flowchart nodes; frame-0 page sec. 2).
- *   q, k, v: [B, H, seq_alloc, D] of `dtype` (bf16 or f32; f32 is rounded
- *            to bf16 for the matrix products).
+ *   q, k, v: [B, H, seq_alloc, D] of `dtype` (bf16 or f32).
  *   kv_cnt, kv_idx: row lists as written by bsa_build_mask (row stride nkb).
  *            Indices outside [0, nkb) are skipped.
  *   log_w:   NULL or [B, H, nqb, nkb] float32 per-slot log-weights.
@@ -203,8 +202,9 @@ bsa_status bsa_build_mask(const float* q_pooled, const float* k_pooled, const bs
  *   For query token t of block i: o_t = sum_u softmax_u(q_t·k_u * scale +
  *   log_w[i][p(u)]) v_u over the tokens u < S of the listed key blocks
  *   (p(u) = list slot of u's block); key blocks smaller than 64 tokens are
- *   gathered four/two per 64-key tile.  bf16 matrix products, float32
- *   accumulation and softmax.
+ *   gathered four/two per 64-key tile.  bf16: bf16 matrix products with
+ *   float32 accumulation and softmax (P rounded to bf16 for the P V
+ *   product); f32: float32 matrix products and softmax throughout.
  *   out:     [B, H, seq_alloc, D] of `dtype`; rows >= S and rows with an
  *            empty list are written as 0.
  *   lse:     NULL or [B, H, seq_alloc] float32, ln sum_u exp(logit_u);

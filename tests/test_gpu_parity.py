@@ -22,7 +22,15 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 bsa = pytest.importorskip("block_sparse_attention_42_amd")
 
-MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3          # bf16 inputs: bf16 products, float32 accumulation
+
+
+def tolerances(w):
+    """(max-abs, mean-abs, LSE atol) against the float64 oracle: the bf16
+    bounds above for bf16 inputs; float32 inputs run float32 products and
+    softmax, whose rounding (logits of magnitude <= 30 at 2^-24 relative,
+    one-ulp exponentials) stays far below 1e-5."""
+    return (MAX_ABS, MEAN_ABS, 2e-3) if w.dtype == "bf16" else (1e-5, 1e-6, 1e-5)
 
 
 def _say(msg):
@@ -92,6 +100,7 @@ def _check_lists(w, r, om, ocnt, oidx, ologw, rows):
 
 
 def _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qblocks_by_head):
+    max_abs, mean_abs, lse_tol = tolerances(w)
     errs = []
     for (b, h), qbl in qblocks_by_head.items():
         o, l = oracle.attention_head(q[b, h], k[b, h], v[b, h], g, ocnt[b, h], oidx[b, h], ologw[b, h],
@@ -101,16 +110,19 @@ def _check_out(w, r, q, k, v, g, ocnt, oidx, ologw, qblocks_by_head):
         assert np.isfinite(got).all()
         err = np.abs(got - o)
         errs.append(err)
-        assert err.max() <= MAX_ABS, (w.name, b, h, err.max())
+        assert err.max() <= max_abs, (w.name, b, h, err.max())
         valid = rows < g.S
         gl = r["lse"][b, h, rows]
         assert np.all(np.isneginf(gl[~valid]))
-        tol = 2e-3 if w.dtype == "bf16" else 5e-2     # float32 inputs are rounded to bf16 on the GPU
-        assert np.allclose(gl[valid], l[valid], atol=tol, rtol=1e-4), (w.name, b, h)
+        fin = np.isfinite(l[valid])
+        assert np.array_equal(np.isfinite(gl[valid]), fin), (w.name, b, h)     # empty rows: -inf on both sides
+        lse_rtol = 1e-4 if w.dtype == "bf16" else 1e-6
+        assert np.all(np.abs(gl[valid][fin] - l[valid][fin]) <= lse_tol + lse_rtol * np.abs(l[valid][fin])), \
+            (w.name, b, h)
         assert np.all(got[~valid] == 0)
     allerr = np.concatenate([e.ravel() for e in errs])
     _say(f"    out max|err| {allerr.max():.3e} mean|err| {allerr.mean():.3e} over {allerr.size} values")
-    assert allerr.mean() <= MEAN_ABS
+    assert allerr.mean() <= mean_abs
 
 
 SMALL = {
@@ -260,7 +272,7 @@ def test_forward_arbitrary_lists_weights_and_nan_pads():
                               torch.from_numpy(lw).cuda(), softmax_scale=0.05)
     torch.cuda.synchronize()
     o, _ = oracle.attention_head(q[0, 0], k[0, 0], v[0, 0], g, cnt[0, 0], idx[0, 0], lw[0, 0], softmax_scale=0.05)
-    assert np.abs(out2.float().cpu().numpy()[0, 0, :o.shape[0]] - o).max() <= MAX_ABS
+    assert np.abs(out2.float().cpu().numpy()[0, 0, :o.shape[0]] - o).max() <= tolerances(w)[0]
 
 
 def test_deterministic_reruns():
