@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn fwd ms/call + effective TFLOP/s (frac of MFMA peak) at 90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3     # MI355X dense float32 MFMA (the float32 forward)
 PEAK_HBM_GBS = 8000.0
 # fp32 vector lane-ops without packed math: 256 CUs x 4 SIMDs x 16 lanes per clock at 2.4 GHz
 PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -60,13 +61,16 @@ def _args():
     return ap.parse_args()
 
 
-FWD_SOURCES = ("forward.hip", "forward_wide.hip", "fwd_common.h")
+FWD_SOURCES = ("forward.hip", "forward_wide.hip", "forward_f32.hip", "fwd_common.h")
 
 
 def fwd_kernel_of(w):
-    """The forward kernel a workload runs: the 64-key-step kernel for bf16,
-    head_dim 128, 64-row query blocks; the general kernel otherwise."""
-    wide = w.dtype == "bf16" and w.D == 128 and w.q_block == 64 and w.k_block in (16, 32, 64)
+    """The forward kernel a workload runs: the float32 kernel for float32
+    inputs; for bf16 the 64-key-step kernel at head_dim 128 with 64-row query
+    blocks, the general kernel otherwise."""
+    if w.dtype != "bf16":
+        return "fwd_f32_kernel"
+    wide = w.D == 128 and w.q_block == 64 and w.k_block in (16, 32, 64)
     return "fwd_wide_kernel" if wide else "fwd_kernel"
 
 
@@ -427,6 +431,7 @@ class PathRun:
         """Per-workload figures: forward, pooling and mask times and their roofline fractions."""
         w = self.w
         kernel = fwd_kernel_of(w)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
         tf = self.flops / (m["fwd_ms"] * 1e-3) / 1e12
         tf_avg = self.flops / (m["fwd_ms_mean"] * 1e-3) / 1e12
         pool_gbs = m["pool_bytes"] / (m["pool_ms"] * 1e-3) / 1e9
@@ -437,7 +442,7 @@ class PathRun:
                 "ms_per_step": round(m["step_ms"], 4),
                 "step_tflops": round(self.flops / (m["step_ms"] * 1e-3) / 1e12, 2),
                 "fwd_kernel": kernel, "fwd_ms": round(m["fwd_ms"], 4), "fwd_ms_mean": round(m["fwd_ms_mean"], 4),
-                "fwd_tflops": round(tf, 2), "fwd_frac": round(tf_avg / PEAK_BF16_TFLOPS, 4),
+                "fwd_tflops": round(tf, 2), "fwd_frac": round(tf_avg / peak, 4), "fwd_peak_tflops": peak,
                 "fwd_hbm_bytes": _profile_record("traffic", kernel, w.name, "hbm_bytes_per_launch"),
                 "pool_ms": round(m["pool_ms"], 4), "pool_gbs": round(pool_gbs, 1),
                 "pool_frac": round(pool_gbs / PEAK_HBM_GBS, 4),

@@ -76,39 +76,68 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void fwd_f32_ker
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
   }
 
+  // list entry and log-weight of part b of sub-tile u (entry -1 past the list)
+  auto entry = [&](int u, int b, int& j, float& w) {
+    const int pos = (u * SUB + b * PART) / BK;
+    j = pos < cnt ? lst[pos] : -1;
+    w = (pos < cnt && lw) ? lw[pos] : 0.0f;
+  };
+  int nj[NBLK];
+  float nw[NBLK];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) entry(0, b, nj[b], nw[b]);
   for (int u = 0; u < nsub; ++u) {
-    // the list entries of the sub-tile: first key, valid keys, log2 weight
+    // the list entries of the sub-tile (fetched one sub-tile ahead): first
+    // key, valid keys, log2 weight
     int key0[NBLK], valid[NBLK];
     float bias[NBLK];
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
       const int g = u * SUB + b * PART;
-      const int pos = g / BK;
+      const int j = nj[b];
       key0[b] = 0;
       valid[b] = 0;
       bias[b] = 0.0f;
-      if (pos < cnt) {
-        const int j = lst[pos];
-        if ((uint32_t)j < (uint32_t)a.nkb) {
-          key0[b] = j * BK + g % BK;
-          const int64_t rest = a.S - key0[b];
-          valid[b] = rest < PART ? (rest > 0 ? (int)rest : 0) : PART;
-          bias[b] = lw ? lw[pos] * 1.4426950408889634f : 0.0f;
-        }
+      if ((uint32_t)j < (uint32_t)a.nkb) {
+        key0[b] = j * BK + g % BK;
+        const int64_t rest = a.S - key0[b];
+        valid[b] = rest < PART ? (rest > 0 ? (int)rest : 0) : PART;
+        bias[b] = nw[b] * 1.4426950408889634f;
       }
     }
-    // S^T: key row qc of the tile in the A operand
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b) entry(u + 1, b, nj[b], nw[b]);
+    // the sub-tile's K and V operands, all loads issued before the first
+    // product so that their latencies overlap: key row qc of the tile in the
+    // S^T A operand; for the P V products, the keys of register t
     const int kp = qc / PART, ko = qc % PART;
     const bool kvalid = ko < valid[kp];
     const float* krow = Kb + (int64_t)(key0[kp] + ko) * D;
+    float kv[DS];
+#pragma unroll
+    for (int st = 0; st < DS; ++st) kv[st] = kvalid ? krow[2 * st + hf] : 0.0f;
+    // (V ahead of the products where the registers allow: not for 64 rows
+    // at head_dim 128, whose Q and O already take 256 of them)
+    constexpr bool kVAhead = D * QT <= 128;
+    auto v_of = [&](int t, int dt) {
+      const int i = 8 * (t >> 2) + 4 * hf + (t & 3);
+      const int ip = i / PART, io = i % PART;
+      return io < valid[ip] ? Vb[(int64_t)(key0[ip] + io) * D + 32 * dt + qc] : 0.0f;
+    };
+    float vv[kVAhead ? 16 : 1][DT];
+    if constexpr (kVAhead) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vv[t][dt] = v_of(t, dt);
+    }
     f32x16 s[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) s[qt] = f32x16{};
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
-      const float kv = kvalid ? krow[2 * st + hf] : 0.0f;
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[qt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, qf[qt][st], s[qt], 0, 0, 0);
+      for (int qt = 0; qt < QT; ++qt) s[qt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[st], qf[qt][st], s[qt], 0, 0, 0);
     }
     // log2-domain logits of this lane's 16 keys; keys past the valid ones -inf
     float p[QT][16];
@@ -141,19 +170,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void fwd_f32_ker
     // O^T += V^T P^T: step t pairs key 8(t/4) + t%4 (lanes 0-31) with key
     // 8(t/4) + 4 + t%4 (lanes 32-63), the keys of register t
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int i = 8 * (t >> 2) + 4 * hf + (t & 3);
-      const int ip = i / PART, io = i % PART;
-      const bool ok = io < valid[ip];
-      const float* vrow = Vb + (int64_t)(key0[ip] + io) * D;
+    for (int t = 0; t < 16; ++t)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const float vv = ok ? vrow[32 * dt + qc] : 0.0f;
+        const float v = kVAhead ? vv[kVAhead ? t : 0][dt] : v_of(t, dt);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, p[qt][t], o[qt][dt], 0, 0, 0);
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v, p[qt][t], o[qt][dt], 0, 0, 0);
       }
-    }
   }
 
   // ---- epilogue: normalize (or leave the partial state of a split row) ----
