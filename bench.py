@@ -61,7 +61,11 @@ def _args():
     return ap.parse_args()
 
 
-FWD_SOURCES = ("forward.hip", "forward_wide.hip", "forward_f32.hip", "fwd_common.h")
+# the sources (and their compile flags) that make each forward kernel: the
+# digest a committed profile was taken under
+FWD_SOURCES = {"fwd_wide_kernel": ("forward_wide.hip", "fwd_common.h"),
+               "fwd_kernel": ("forward.hip", "fwd_common.h"),
+               "fwd_f32_kernel": ("forward_f32.hip", "fwd_common.h")}
 
 
 def fwd_kernel_of(w):
@@ -74,12 +78,12 @@ def fwd_kernel_of(w):
     return "fwd_wide_kernel" if wide else "fwd_kernel"
 
 
-def code_digest(names=FWD_SOURCES):
-    """sha256 of the forward's HIP sources with `//` comments and blank lines
-    removed, plus their compile flags (the code the counters measured)."""
+def code_digest(kernel):
+    """sha256 of a forward kernel's HIP sources with `//` comments and blank
+    lines removed, plus their compile flags (the code the counters measured)."""
     from block_sparse_attention_42_amd.build import COMMON, EXTRA
     out = []
-    for name in names:
+    for name in FWD_SOURCES[kernel]:
         for line in open(os.path.join(ROOT, "block_sparse_attention_42_amd", "csrc", name), encoding="utf-8"):
             code = line.split("//", 1)[0].rstrip()
             if code:
@@ -95,7 +99,7 @@ def _profile_record(kind, kernel, name, field):
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
-    if rec.get("forward_code_sha256") != code_digest():
+    if rec.get("forward_code_sha256") != code_digest(kernel):
         return None
     return rec.get(field)
 
