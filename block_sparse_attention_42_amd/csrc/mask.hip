@@ -496,16 +496,18 @@ std::atomic<uint32_t> g_mask_lds_raised[kMaxDevices];   // per device: bit per (
 
 template <int R, int JT, bool SAMPLE>
 hipError_t launch_rj(const MaskArgs& a, size_t lds, unsigned grid, hipStream_t stream) {
-  const void* f = reinterpret_cast<const void*>(&mask_kernel<R, JT, SAMPLE>);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const uint32_t bit = 1u << (4 * (SAMPLE ? 1 : 0) + 2 * (R == 8 ? 1 : 0) + (JT == 1 ? 0 : 1));
-  const bool known = dev >= 0 && dev < kMaxDevices;
-  if (lds > 64 * 1024 && (!known || !(g_mask_lds_raised[dev].load(std::memory_order_acquire) & bit))) {
-    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaskLdsCap);
+  if (lds > 64 * 1024) {   // above the default dynamic LDS limit: raise it once per device
+    const void* f = reinterpret_cast<const void*>(&mask_kernel<R, JT, SAMPLE>);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (known) g_mask_lds_raised[dev].fetch_or(bit, std::memory_order_release);
+    const uint32_t bit = 1u << (4 * (SAMPLE ? 1 : 0) + 2 * (R == 8 ? 1 : 0) + (JT == 1 ? 0 : 1));
+    const bool known = dev >= 0 && dev < kMaxDevices;
+    if (!known || !(g_mask_lds_raised[dev].load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaskLdsCap);
+      if (e != hipSuccess) return e;
+      if (known) g_mask_lds_raised[dev].fetch_or(bit, std::memory_order_release);
+    }
   }
   hipLaunchKernelGGL((mask_kernel<R, JT, SAMPLE>), dim3(grid), dim3(kMaskThreads), lds, stream, a);
   return hipGetLastError();
