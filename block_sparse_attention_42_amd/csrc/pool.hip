@@ -126,6 +126,100 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolJobs jobs) {
   }
 }
 
+// bf16: one wave per span of kSpan consecutive rows of one head (contiguous in
+// memory, at most 16 KB; spans start on block boundaries since every block
+// size divides kSpan).  The wave reads its span with 16-byte coalesced
+// non-temporal loads (each instruction 1 KB of consecutive bytes), stages it
+// in LDS, and then lane l adds channels l*CPL .. l*CPL+CPL-1 (CPL = D/64) of
+// each block of the span over its rows in ascending order.  Against the
+// per-lane kernel (each load instruction two 256-byte rows 16 KB apart) this
+// measured 22 % faster for the 201 MB of Q and K at the Wan-like shape on
+// MI355X (0.049 -> 0.0385 ms) and 1.5 % at the HunyuanVideo-like one.
+constexpr int kSpan = 64;
+constexpr int kSpanBytes = kSpan * 128 * 2;
+
+// The block means of one staged span: rows of a full block unrolled (their
+// LDS reads issued ahead of the adds), the short last block of a head by a
+// loop; the adds in ascending row order either way.
+template <int kBlock>
+__device__ __forceinline__ void span_sums(const PoolArgs& a, const uint32_t* st, int nrow, int64_t row0, int lane) {
+#pragma unroll
+  for (int r0 = 0; r0 < kSpan; r0 += kBlock) {
+    if (r0 >= nrow) break;
+    const int n = min(kBlock, nrow - r0);
+    const float fn = (float)n;
+    float* out = a.out + (row0 + r0 / kBlock) * a.D;
+    if (a.D == 128) {
+      float acc0 = 0.0f, acc1 = 0.0f;
+      const uint32_t* sw = st + r0 * 64 + lane;
+      auto add = [&](uint32_t x) {
+        acc0 = __fadd_rn(acc0, __uint_as_float(x << 16));
+        acc1 = __fadd_rn(acc1, __uint_as_float(x & 0xffff0000u));
+      };
+      if (n == kBlock) {
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) add(sw[t * 64]);
+      } else {
+        for (int t = 0; t < n; ++t) add(sw[t * 64]);
+      }
+      float2 o;
+      o.x = __fdiv_rn(acc0, fn);
+      o.y = __fdiv_rn(acc1, fn);
+      *reinterpret_cast<float2*>(out + 2 * lane) = o;
+    } else {   // D = 64: one channel a lane
+      const uint16_t* sh = reinterpret_cast<const uint16_t*>(st) + r0 * 64 + lane;
+      float acc = 0.0f;
+      if (n == kBlock) {
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) acc = __fadd_rn(acc, __uint_as_float((uint32_t)sh[t * 64] << 16));
+      } else {
+        for (int t = 0; t < n; ++t) acc = __fadd_rn(acc, __uint_as_float((uint32_t)sh[t * 64] << 16));
+      }
+      out[lane] = __fdiv_rn(acc, fn);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kPoolThreads) void pool_span_kernel(PoolJobs jobs) {
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kPoolThreads / 64][kSpanBytes / 4];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int j = (int64_t)blockIdx.x >= jobs.first[1] ? 1 : 0;
+  const PoolArgs& a = jobs.job[j];
+  const int64_t nspan = (a.S + kSpan - 1) / kSpan;        // spans per head
+  const int64_t sp = ((int64_t)blockIdx.x - jobs.first[j]) * (kPoolThreads / 64) + wave;
+  if (sp >= (int64_t)a.BH * nspan) return;
+  const int64_t bh = sp / nspan;
+  const int64_t t0 = (sp % nspan) * kSpan;
+  const int nrow = (int)min<int64_t>(kSpan, a.S - t0);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t* src =
+      reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(a.x) + (bh * a.seq_alloc + t0) * a.D);
+  const int chunks = nrow * a.D / 8;                       // 16-byte chunks of the span's valid rows
+  constexpr int kPer = kSpanBytes / 16 / 64;               // chunks per lane (D = 128)
+  u32x4_t r[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k;
+    if (c < chunks) r[k] = __builtin_nontemporal_load(src + c);
+  }
+  u32x4_t* st = reinterpret_cast<u32x4_t*>(stage[wave]);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k;
+    if (c < chunks) st[c] = r[k];
+  }
+  // the lanes read what other lanes of the wave wrote
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int64_t row0 = bh * a.nb + t0 / a.block;           // first pooled row of the span
+  switch (a.block) {
+    case 16: span_sums<16>(a, stage[wave], nrow, row0, lane); break;
+    case 32: span_sums<32>(a, stage[wave], nrow, row0, lane); break;
+    default: span_sums<64>(a, stage[wave], nrow, row0, lane); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool_jobs(const PoolArgs* jobs, int njobs, int dtype, hipStream_t stream) {
@@ -142,10 +236,18 @@ hipError_t launch_pool_jobs(const PoolArgs* jobs, int njobs, int dtype, hipStrea
     }
   }
   if (njobs == 1) pj.first[1] = INT64_MAX;
-  if (dtype == 0)
-    hipLaunchKernelGGL(pool_kernel<bf16_t>, dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, pj);
-  else
+  if (dtype == 0) {
+    // bf16: the span kernel, four spans per workgroup
+    int64_t g = 0;
+    for (int j = 0; j < 2; ++j) {
+      pj.first[j] = g;
+      if (j < njobs) g += ((int64_t)jobs[j].BH * ((jobs[j].S + kSpan - 1) / kSpan) + 3) / 4;
+    }
+    if (njobs == 1) pj.first[1] = INT64_MAX;
+    hipLaunchKernelGGL(pool_span_kernel, dim3((unsigned)g), dim3(kPoolThreads), 0, stream, pj);
+  } else {
     hipLaunchKernelGGL(pool_kernel<float>, dim3((unsigned)grid), dim3(kPoolThreads), 0, stream, pj);
+  }
   return hipGetLastError();
 }
 
