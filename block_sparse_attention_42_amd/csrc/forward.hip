@@ -86,6 +86,8 @@ void fwd_kernel(FwdArgs a) {
   const int part = part_item ? (int)blockIdx.x % a.split : 0;
   const int lo = part_item ? (int)((int64_t)part * cnt_row / a.split) : 0;
   const int cnt = part_item ? (int)((int64_t)(part + 1) * cnt_row / a.split) - lo : cnt_row;
+  // rows past the head's last query block (seq_alloc > nqb * q_block)
+  if (qb == a.nqb - 1 && part == 0) zero_tail_rows<T, D>(a, bh, lane);
   const int nsub = (cnt * BK + SUB - 1) / SUB;          // 32-key sub-tiles of the row
 
   const T* Qb = reinterpret_cast<const T*>(a.q) + (int64_t)bh * a.seq_alloc * D;

@@ -48,6 +48,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void fwd_f32_ker
   const int part = part_item ? (int)blockIdx.x % a.split : 0;
   const int lo = part_item ? (int)((int64_t)part * cnt_row / a.split) : 0;
   const int cnt = part_item ? (int)((int64_t)(part + 1) * cnt_row / a.split) - lo : cnt_row;
+  // rows past the head's last query block (seq_alloc > nqb * q_block)
+  if (qb == a.nqb - 1 && part == 0) zero_tail_rows<float, D>(a, bh, lane);
   const int nsub = (cnt * BK + SUB - 1) / SUB;
 
   const float* Qb = reinterpret_cast<const float*>(a.q) + (int64_t)bh * a.seq_alloc * D;

@@ -183,6 +183,21 @@ __device__ __forceinline__ bool schedule(const FwdArgs& a, int t, int& bh, int& 
   return true;
 }
 
+// Rows [nqb * q_block, seq_alloc) of a head belong to no query block (a
+// caller may allocate more rows than the blocks cover): the work item of the
+// head's last query block writes them as 0 and their LSE as -inf.
+template <typename T, int D>
+__device__ __forceinline__ void zero_tail_rows(const FwdArgs& a, int bh, int lane) {
+  const int64_t t0 = (int64_t)a.nqb * a.q_block;
+  if (t0 >= a.seq_alloc) return;
+  T* Ob = reinterpret_cast<T*>(a.out) + (int64_t)bh * a.seq_alloc * D;
+  uint4* dst = reinterpret_cast<uint4*>(Ob + t0 * D);   // 16-byte aligned: D * sizeof(T) is a multiple of 16
+  const int64_t n = (a.seq_alloc - t0) * D * (int64_t)sizeof(T) / 16;
+  for (int64_t e = lane; e < n; e += 64) dst[e] = make_uint4(0u, 0u, 0u, 0u);
+  if (a.lse)
+    for (int64_t r = t0 + lane; r < a.seq_alloc; r += 64) a.lse[(int64_t)bh * a.seq_alloc + r] = -INFINITY;
+}
+
 // f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
