@@ -17,16 +17,16 @@
 // wave's LDS.  Every block with score >= T is kept.
 //
 // Kernels, in launch order (grid-wide dependencies between them):
-//   tp_row_entropy    one wave per row: sum_j -P log(P + eps) (float64)
+//   tp_row_entropy    one wave per row: sum_j -P log(P + eps) (float64); the
+//                     workgroups past the rows take the norms of the pooled
+//                     value rows (value-aware scores)
 //   tp_head_entropy   one workgroup per head: the mean over its rows
 //   tp_pools          one workgroup per batch element: median split, pool of
 //                     every head, pool state cleared
-//   tp_value_norm     norm of every pooled value row (value-aware scores)
-//   tp_row_total      one wave per pooled row: its mass
-//   tp_pool_target    one workgroup per pool: total, target = ceil(p * total)
 //   tp_hist, tp_digit (x4)  radix passes of the pooled thresholds: integer
-//                     bin masses of 16 rows per workgroup, then per pool a
-//                     suffix scan picks the digit
+//                     bin masses of kRowsPerHist rows per workgroup, then per
+//                     pool a suffix scan picks the digit (the first pass's
+//                     bins add up to the pool's mass, which sets the target)
 //   tp_select         one wave per row: threshold (the pool's, or its own
 //                     radix select), safeguard, frame-0 rows, text columns,
 //                     compaction
@@ -39,10 +39,15 @@ namespace {
 
 constexpr int kTpThreads = 256;
 constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks in registers
+constexpr int kRowsPerHist = 8;    // rows of one head per histogram workgroup
+constexpr int kBatch = 8;          // loads a thread issues before it uses them
+constexpr int kNormRows = 16;      // pooled value rows per norm workgroup
+constexpr int kMaxHeads = 4096;    // heads of a batch element (head entropies in LDS)
 
 struct PoolState {
-  unsigned long long total, target, rem;
-  uint32_t prefix, used;
+  unsigned long long rem;   // mass the digits still to be chosen must cover
+  uint32_t prefix;          // the threshold's order-key digits chosen so far
+  uint32_t used;            // some head belongs to the pool
   unsigned long long bins[256];
 };
 
@@ -57,26 +62,21 @@ __device__ __forceinline__ unsigned long long fixed_mass(float s) {
 
 struct Ws {
   double* row_ent;        // [BH * nqb]
-  unsigned long long* row_tot;   // [BH * nqb]
   double* head_ent;       // [BH]
   int32_t* pool;          // [BH]
-  float* vnorm;           // [BH * nkb]
+  float* vnorm;           // [BH * vstride]
   PoolState* ps;          // [npools]
 };
-
-constexpr int kRowsPerHist = 16;   // rows of one head per histogram workgroup
 
 __device__ __forceinline__ Ws ws_of(const TopPArgs& a) {
   char* p = reinterpret_cast<char*>(a.ws);
   Ws w;
   w.row_ent = reinterpret_cast<double*>(p);
   p += sizeof(double) * (size_t)a.BH * a.nqb;
-  w.row_tot = reinterpret_cast<unsigned long long*>(p);
-  p += sizeof(unsigned long long) * (size_t)a.BH * a.nqb;
   w.head_ent = reinterpret_cast<double*>(p);
   p += sizeof(double) * (size_t)a.BH;
   w.pool = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * (size_t)((a.BH + 1) / 2 * 2);
+  p += sizeof(int32_t) * (size_t)((a.BH + 3) / 4 * 4);
   w.vnorm = reinterpret_cast<float*>(p);
   p += sizeof(float) * (size_t)a.BH * ((a.nkb + 3) / 4 * 4);
   w.ps = reinterpret_cast<PoolState*>(p);
@@ -89,9 +89,70 @@ __device__ __forceinline__ float score_of(const TopPArgs& a, const Ws& w, int bh
   return (a.value_aware && pooled) ? __fmul_rn(s, w.vnorm[(int64_t)bh * a.vstride + j]) : s;
 }
 
-// one wave per row
-__global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a) {
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+// Correctly rounded square root of x >= 0.  The compiler's root may be the
+// hardware's approximate one; it is moved to the float whose rounding
+// interval holds sqrt(x), decided exactly in double: a midpoint of two
+// adjacent floats has at most 25 significant bits, so its square is exact.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  float s = __builtin_sqrtf(x);
+  const double xd = (double)x;
+  for (int it = 0; it < 3; ++it) {
+    const uint32_t u = __float_as_uint(s);
+    const double d = (double)s;
+    const double hi = 0.5 * (d + (double)__uint_as_float(u + 1u));
+    if (xd >= hi * hi) {
+      s = __uint_as_float(u + 1u);
+    } else if (u > 0u) {
+      const double lo = 0.5 * (d + (double)__uint_as_float(u - 1u));
+      if (xd < lo * lo) s = __uint_as_float(u - 1u);
+    }
+  }
+  return s;
+}
+
+// Norms of kNormRows pooled value rows: the rows are staged in LDS by the
+// whole workgroup (coalesced), then one thread per row sums its squares in
+// ascending channel order.
+__device__ void value_norms(const TopPArgs& a, const Ws& w, int g) {
+  __shared__ float rows[kNormRows * (128 + 1)];
+  const int D = a.D, ld = D + 1;
+  const int64_t e0 = (int64_t)g * kNormRows;                 // first row: bh * nkb + j
+  const int64_t nrows = (int64_t)a.BH * a.nkb;
+  const int nr = (int)min((int64_t)kNormRows, nrows - e0);
+  const float4* src = reinterpret_cast<const float4*>(a.vp + e0 * D);
+  for (int c = threadIdx.x; c < nr * D / 4; c += kTpThreads) {
+    const float4 x = src[c];
+    const int r = (4 * c) / D, d = (4 * c) % D;
+    float* dst = rows + r * ld + d;
+    dst[0] = x.x;
+    dst[1] = x.y;
+    dst[2] = x.z;
+    dst[3] = x.w;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nr) {
+    const float* v = rows + threadIdx.x * ld;
+    float acc = 0.0f;
+    for (int d = 0; d < D; ++d) acc = __fadd_rn(acc, __fmul_rn(v[d], v[d]));
+    const int64_t e = e0 + threadIdx.x;
+    const int bh = (int)(e / a.nkb), j = (int)(e % a.nkb);
+    w.vnorm[(int64_t)bh * a.vstride + j] = sqrt_rn(acc);
+  }
+}
+
+// one wave per row; workgroups from ent_groups on compute value norms
+__global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a, int ent_groups) {
   const Ws w = ws_of(a);
+  if ((int)blockIdx.x >= ent_groups) {                       // uniform per workgroup
+    value_norms(a, w, (int)blockIdx.x - ent_groups);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
   if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
@@ -107,6 +168,20 @@ __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a) {
   if (lane == 0) w.row_ent[row] = acc;
 }
 
+// Heads in pool q of batch element b (the median split ranks the H heads
+// 0..H-1, so floor(H/2) of them are low-entropy).
+__device__ __forceinline__ int heads_in_pool(const TopPArgs& a, int b, int q) {
+  const int H = a.H;
+  switch (a.domain) {
+    case 1: return 1;
+    case 2: return q == 2 * b ? H / 2 : H - H / 2;
+    case 3: return H;
+    case 4: return H / 2;
+    default: return 0;
+  }
+}
+
+// one workgroup per head: the mean of its row entropies
 __global__ __launch_bounds__(kTpThreads) void tp_head_entropy(TopPArgs a) {
   __shared__ double red[kTpThreads];
   const Ws w = ws_of(a);
@@ -127,11 +202,14 @@ __global__ __launch_bounds__(kTpThreads) void tp_head_entropy(TopPArgs a) {
   }
 }
 
+// one workgroup per batch element
 __global__ __launch_bounds__(kTpThreads) void tp_pools(TopPArgs a) {
+  __shared__ double hent[kMaxHeads];
   const Ws w = ws_of(a);
   const int b = blockIdx.x;
   const int H = a.H;
-  const double* hent = w.head_ent + (int64_t)b * H;
+  for (int h = threadIdx.x; h < H; h += kTpThreads) hent[h] = w.head_ent[b * H + h];
+  __syncthreads();
   for (int h = threadIdx.x; h < H; h += kTpThreads) {
     int rank = 0;
     for (int o = 0; o < H; ++o) rank += (hent[o] < hent[h] || (hent[o] == hent[h] && o < h)) ? 1 : 0;
@@ -158,86 +236,10 @@ __global__ __launch_bounds__(kTpThreads) void tp_pools(TopPArgs a) {
     PoolState* ps = w.ps + q;
     for (int d = threadIdx.x; d < 256; d += kTpThreads) ps->bins[d] = 0ull;
     if (threadIdx.x == 0) {
-      ps->total = 0ull;
-      ps->target = 0ull;
       ps->rem = 0ull;
       ps->prefix = 0u;
-      ps->used = 0u;
+      ps->used = heads_in_pool(a, b, q) > 0 ? 1u : 0u;
     }
-  }
-}
-
-__global__ __launch_bounds__(kTpThreads) void tp_value_norm(TopPArgs a) {
-  const Ws w = ws_of(a);
-  const int64_t e = (int64_t)blockIdx.x * kTpThreads + threadIdx.x;   // bh * nkb + j
-  if (e >= (int64_t)a.BH * a.nkb) return;
-  const int bh = (int)(e / a.nkb), j = (int)(e % a.nkb);
-  const float* v = a.vp + e * a.D;
-  // the loads are independent (16 bytes each, all issued up front); the sum
-  // is the ascending-channel chain
-  float acc = 0.0f;
-  auto chain = [&](auto dn) {
-    constexpr int DN = decltype(dn)::value;
-    float4 x[DN / 4];
-#pragma unroll
-    for (int c = 0; c < DN / 4; ++c) x[c] = *reinterpret_cast<const float4*>(v + 4 * c);
-#pragma unroll
-    for (int c = 0; c < DN / 4; ++c) {
-      acc = __fadd_rn(acc, __fmul_rn(x[c].x, x[c].x));
-      acc = __fadd_rn(acc, __fmul_rn(x[c].y, x[c].y));
-      acc = __fadd_rn(acc, __fmul_rn(x[c].z, x[c].z));
-      acc = __fadd_rn(acc, __fmul_rn(x[c].w, x[c].w));
-    }
-  };
-  if (a.D == 128) chain(std::integral_constant<int, 128>{});
-  else chain(std::integral_constant<int, 64>{});
-  w.vnorm[(int64_t)bh * a.vstride + j] = __fsqrt_rn(acc);
-}
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-  return v;
-}
-
-__global__ __launch_bounds__(kTpThreads) void tp_row_total(TopPArgs a) {
-  const Ws w = ws_of(a);
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.BH * a.nqb) return;                  // uniform per wave
-  const int bh = (int)(row / a.nqb);
-  if (w.pool[bh] < 0) return;
-  unsigned long long acc = 0ull;
-  for (int j = lane; j < a.nkb; j += 64) acc += fixed_mass(score_of(a, w, bh, row, j, true));
-  acc = wave_sum_u64(acc);
-  if (lane == 0) w.row_tot[row] = acc;
-}
-
-__global__ __launch_bounds__(kTpThreads) void tp_pool_target(TopPArgs a) {
-  __shared__ unsigned long long red[kTpThreads];
-  const Ws w = ws_of(a);
-  const int q = blockIdx.x;
-  unsigned long long acc = 0ull;
-  int mine = 0;
-  for (int bh = 0; bh < a.BH; ++bh) {
-    if (w.pool[bh] != q) continue;                           // uniform
-    const unsigned long long* rt = w.row_tot + (int64_t)bh * a.nqb;
-    for (int i = threadIdx.x; i < a.nqb; i += kTpThreads) acc += rt[i];
-    ++mine;
-  }
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int h = kTpThreads / 2; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    PoolState* ps = w.ps + q;
-    ps->used = mine > 0 ? 1u : 0u;
-    ps->total = red[0];
-    ps->target = (unsigned long long)ceil(a.top_p * (double)red[0]);
-    ps->rem = ps->target;
-    ps->prefix = 0u;
   }
 }
 
@@ -248,22 +250,42 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
   const int bh = blockIdx.x / groups;
   const int i0 = (blockIdx.x % groups) * kRowsPerHist;
   const int pid = w.pool[bh];
-  if (pid < 0) return;
+  if (pid < 0) return;                                       // uniform: the head is in no pool
+  PoolState* ps = w.ps + pid;
   bins[threadIdx.x] = 0ull;
   __syncthreads();
-  const uint32_t prefix = w.ps[pid].prefix;
+  const uint32_t prefix = ps->prefix;
   const int i1 = min(i0 + kRowsPerHist, a.nqb);
+  const int n = (i1 - i0) * a.nkb;                           // the rows' scores, contiguous
+  const float* base = a.scores + ((int64_t)bh * a.nqb + i0) * a.nkb;
+  const float* vn = w.vnorm + (int64_t)bh * a.vstride;
   // most scores share their leading digits: a thread adds up a run of equal
   // digits itself and makes one LDS atomic per run (integer sums: exact in
   // any order)
   uint32_t cur = 256u;
   unsigned long long acc = 0ull;
-  for (int i = i0; i < i1; ++i) {
-    const int64_t row = (int64_t)bh * a.nqb + i;
-    for (int j = threadIdx.x; j < a.nkb; j += kTpThreads) {
-      const float s = score_of(a, w, bh, row, j, true);
-      const uint32_t k = okey(s);
-      const bool match = shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u;
+  for (int e0 = 0; e0 < n; e0 += kTpThreads * kBatch) {
+    float sv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + kTpThreads * u + (int)threadIdx.x;
+      sv[u] = e < n ? base[e] : 0.0f;
+    }
+    if (a.value_aware) {
+      int j = (e0 + (int)threadIdx.x) % a.nkb;              // key block of element u
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + kTpThreads * u + (int)threadIdx.x;
+        if (e < n) sv[u] = __fmul_rn(sv[u], vn[j]);
+        j += kTpThreads;
+        while (j >= a.nkb) j -= a.nkb;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + kTpThreads * u + (int)threadIdx.x;
+      const uint32_t k = okey(sv[u]);
+      const bool match = e < n && (shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u);
       if (match) {
         const uint32_t b = (k >> shift) & 255u;
         if (b != cur) {
@@ -271,19 +293,21 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
           cur = b;
           acc = 0ull;
         }
-        acc += fixed_mass(s);
+        acc += fixed_mass(sv[u]);
       }
     }
   }
   if (acc) atomicAdd(&bins[cur], acc);
   __syncthreads();
   const unsigned long long v = bins[threadIdx.x];
-  if (v) atomicAdd(&w.ps[pid].bins[threadIdx.x], v);
+  if (v) atomicAdd(&ps->bins[threadIdx.x], v);
 }
 
-// per pool: suffix sums of the bins (mass of digits >= d inside the current
+// Per pool: suffix sums of the bins (mass of digits >= d inside the current
 // prefix group); the digit is the largest d whose suffix reaches the
-// remaining target, and the mass of the larger digits leaves the target
+// remaining target, and the mass of the larger digits leaves the target.  In
+// the first pass the bins hold the whole pool, so their sum is the pool's
+// mass and the target is ceil(p * mass).
 __global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
   __shared__ unsigned long long suf[257];
   const Ws w = ws_of(a);
@@ -299,8 +323,8 @@ __global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
     suf[d] += v;
     __syncthreads();
   }
-  const unsigned long long rem = ps->rem;
-  __syncthreads();
+  const unsigned long long rem = shift == 24 ? (unsigned long long)ceil(a.top_p * (double)suf[0]) : ps->rem;
+  __syncthreads();                                           // every thread has read rem before it changes
   if (suf[d] >= rem && suf[d + 1] < rem) {
     ps->rem = rem - suf[d + 1];
     ps->prefix |= (uint32_t)d << shift;
@@ -483,25 +507,20 @@ __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
 
 int64_t topp_workspace_bytes(int64_t BH, int64_t B, int64_t nqb, int64_t nkb) {
   const int64_t npools = BH > 2 * B ? BH : 2 * B;
-  return (int64_t)sizeof(double) * BH * nqb + (int64_t)sizeof(unsigned long long) * BH * nqb +
-         (int64_t)sizeof(double) * BH +
-         (int64_t)sizeof(int32_t) * ((BH + 1) / 2 * 2) + (int64_t)sizeof(float) * BH * ((nkb + 3) / 4 * 4) +
+  return (int64_t)sizeof(double) * BH * nqb + (int64_t)sizeof(double) * BH +
+         (int64_t)sizeof(int32_t) * ((BH + 3) / 4 * 4) + (int64_t)sizeof(float) * BH * ((nkb + 3) / 4 * 4) +
          (int64_t)sizeof(PoolState) * npools;
 }
 
 hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
   const unsigned wave_groups = (unsigned)(((int64_t)a.BH * a.nqb + 3) / 4);
-  hipLaunchKernelGGL(tp_row_entropy, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
+  const unsigned norm_groups =
+      a.value_aware && a.domain != 0 ? (unsigned)(((int64_t)a.BH * a.nkb + kNormRows - 1) / kNormRows) : 0u;
+  hipLaunchKernelGGL(tp_row_entropy, dim3(wave_groups + norm_groups), dim3(kTpThreads), 0, stream, a,
+                     (int)wave_groups);
   hipLaunchKernelGGL(tp_head_entropy, dim3((unsigned)a.BH), dim3(kTpThreads), 0, stream, a);
   hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
-  if (a.value_aware) {
-    const int64_t n = (int64_t)a.BH * a.nkb;
-    hipLaunchKernelGGL(tp_value_norm, dim3((unsigned)((n + kTpThreads - 1) / kTpThreads)), dim3(kTpThreads), 0,
-                       stream, a);
-  }
   if (a.domain != 0) {
-    hipLaunchKernelGGL(tp_row_total, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
-    hipLaunchKernelGGL(tp_pool_target, dim3((unsigned)a.npools), dim3(kTpThreads), 0, stream, a);
     const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + kRowsPerHist - 1) / kRowsPerHist));
     for (int shift = 24; shift >= 0; shift -= 8) {
       hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, shift);

@@ -74,7 +74,7 @@ def _check(w, P, vp, domain, value_aware, p, frame0, text):
     np.testing.assert_allclose(ent.cpu().numpy(), oent, rtol=1e-9)
     srt = np.sort(oent, axis=1)
     H = g.H
-    if H >= 2:                                    # the split is unambiguous on these inputs
+    if H >= 2 and domain in ("split", "eg"):      # the split is unambiguous on these inputs
         assert (srt[:, H // 2] - srt[:, H // 2 - 1] > 1e-6 * np.abs(srt).max()).all()
     assert np.array_equal(mask.cpu().numpy().astype(bool), om), domain
     c = cnt.cpu().numpy()
@@ -132,6 +132,19 @@ def test_eg_routing_full_size():
     q, k, v = inputs_of(w)
     g, qd, kd, vd, P, vp = _scores(w, q, k, v)
     _check(w, P, vp, "eg", True, 0.9, frame0=True, text=False)
+
+
+def test_value_aware_pools_large_rows():
+    """Per-head pools with value-aware scores at the HunyuanVideo-like shape
+    (rows of about 1700 blocks), every row.  The value norms must be the
+    correctly rounded float32 roots the oracle takes: with the hardware's
+    approximate root, 5 of the 24 heads' thresholds moved by one key."""
+    w = W.workload("hunyuan_keep08")
+    _say("[gpu] top-p full-size per-head value-aware (HunyuanVideo-like)")
+    q, k, v = inputs_of(w)
+    g, qd, kd, vd, P, vp = _scores(w, q, k, v)
+    del q, k, v, qd, kd, vd
+    _check(w, P, vp, "head", True, 0.9, frame0=False, text=False)
 
 
 @pytest.mark.parametrize("domain", ["row", "eg"])
