@@ -23,13 +23,15 @@
 //   tp_head_entropy   one workgroup per head: the mean over its rows
 //   tp_pools          one workgroup per batch element: median split, pool of
 //                     every head, pool state cleared
-//   tp_hist, tp_digit (x4)  radix passes of the pooled thresholds: integer
-//                     bin masses of kRowsPerHist rows per workgroup, then per
-//                     pool a suffix scan picks the digit (the first pass's
-//                     bins add up to the pool's mass, which sets the target)
-//   tp_select         one wave per row: threshold (the pool's, or its own
-//                     radix select), safeguard, frame-0 rows, text columns,
-//                     compaction
+//   tp_hist (x4)      radix passes of the pooled thresholds: integer bin
+//                     masses of kRowsPerHist rows per workgroup, each pass
+//                     into its own bins; a pass starts by deriving the digits
+//                     of the passes before it from their bins (every wave, the
+//                     same suffix scans), and the first pass's bins add up to
+//                     the pool's mass, which sets the target
+//   tp_select         one wave per row: threshold (the pool's, derived from
+//                     its four bin sets, or the row's own radix select),
+//                     safeguard, frame-0 rows, text columns, compaction
 #include <type_traits>
 
 #include "bsa_internal.h"
@@ -45,10 +47,7 @@ constexpr int kNormRows = 16;      // pooled value rows per norm workgroup
 constexpr int kMaxHeads = 4096;    // heads of a batch element (head entropies in LDS)
 
 struct PoolState {
-  unsigned long long rem;   // mass the digits still to be chosen must cover
-  uint32_t prefix;          // the threshold's order-key digits chosen so far
-  uint32_t used;            // some head belongs to the pool
-  unsigned long long bins[256];
+  unsigned long long bins[4][256];   // integer bin masses of each radix pass
 };
 
 __device__ __forceinline__ uint32_t okey(float s) {
@@ -87,12 +86,6 @@ __device__ __forceinline__ Ws ws_of(const TopPArgs& a) {
 __device__ __forceinline__ float score_of(const TopPArgs& a, const Ws& w, int bh, int64_t row, int j, bool pooled) {
   const float s = a.scores[row * a.nkb + j];
   return (a.value_aware && pooled) ? __fmul_rn(s, w.vnorm[(int64_t)bh * a.vstride + j]) : s;
-}
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-  return v;
 }
 
 // Correctly rounded square root of x >= 0.  The compiler's root may be the
@@ -168,19 +161,6 @@ __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a, int ent
   if (lane == 0) w.row_ent[row] = acc;
 }
 
-// Heads in pool q of batch element b (the median split ranks the H heads
-// 0..H-1, so floor(H/2) of them are low-entropy).
-__device__ __forceinline__ int heads_in_pool(const TopPArgs& a, int b, int q) {
-  const int H = a.H;
-  switch (a.domain) {
-    case 1: return 1;
-    case 2: return q == 2 * b ? H / 2 : H - H / 2;
-    case 3: return H;
-    case 4: return H / 2;
-    default: return 0;
-  }
-}
-
 // one workgroup per head: the mean of its row entropies
 __global__ __launch_bounds__(kTpThreads) void tp_head_entropy(TopPArgs a) {
   __shared__ double red[kTpThreads];
@@ -233,17 +213,68 @@ __global__ __launch_bounds__(kTpThreads) void tp_pools(TopPArgs a) {
     default: lo = hi = 0; break;
   }
   for (int q = lo; q < hi; ++q) {
-    PoolState* ps = w.ps + q;
-    for (int d = threadIdx.x; d < 256; d += kTpThreads) ps->bins[d] = 0ull;
-    if (threadIdx.x == 0) {
-      ps->rem = 0ull;
-      ps->prefix = 0u;
-      ps->used = heads_in_pool(a, b, q) > 0 ? 1u : 0u;
-    }
+    unsigned long long* bins = &w.ps[q].bins[0][0];
+    for (int d = threadIdx.x; d < 4 * 256; d += kTpThreads) bins[d] = 0ull;
   }
 }
 
-__global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
+// Digit of one radix pass, by one wave: v[b] is the mass of digit 4 lane + b
+// inside the current prefix group.  Suffix sums (mass of digits >= d); the
+// digit is the largest d whose suffix reaches rem, and the mass of the larger
+// digits leaves rem.  In the first pass the bins hold the whole domain, so
+// their sum is its mass and rem starts at ceil(p * mass).
+__device__ __forceinline__ int wave_digit(unsigned long long (&v)[4], unsigned long long& rem, bool first,
+                                          double top_p, int lane) {
+  v[2] += v[3];
+  v[1] += v[2];
+  v[0] += v[1];
+  unsigned long long above = 0ull;                           // digits of the lanes above
+  unsigned long long x = v[0];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_down(x, o, 64);
+    if (lane + o < 64) {
+      above += y;
+      x += y;
+    }
+  }
+  if (first) rem = (unsigned long long)ceil(top_p * (double)__shfl(x, 0, 64));
+  // x: suffix from digit 4l on; above: from digit 4l + 4 on
+  int dig = -1;
+  unsigned long long past = 0ull;
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    const unsigned long long sb = v[b] + above;                        // digits >= 4l + b
+    const unsigned long long sn = (b == 3 ? 0ull : v[b + 1]) + above;  // digits >= 4l + b + 1
+    if (dig < 0 && sb >= rem && sn < rem) {
+      dig = 4 * lane + b;
+      past = sn;
+    }
+  }
+  const uint64_t who = __ballot(dig >= 0);
+  if (who == 0ull) return 0;                                 // only an empty domain (never a pool in use)
+  const int src = (int)__builtin_ctzll(who);
+  dig = __shfl(dig, src, 64);
+  rem -= __shfl(past, src, 64);
+  return dig;
+}
+
+// The order-key digits of a pool's threshold chosen by its first `passes`
+// radix passes (every wave that needs them derives them from the bins).
+__device__ __forceinline__ uint32_t pool_prefix(const TopPArgs& a, const PoolState* ps, int passes, int lane) {
+  uint32_t prefix = 0u;
+  unsigned long long rem = 0ull;
+  for (int d = 0; d < passes; ++d) {
+    unsigned long long v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = ps->bins[d][4 * lane + b];
+    prefix |= (uint32_t)wave_digit(v, rem, d == 0, a.top_p, lane) << (24 - 8 * d);
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int pass) {
+  const int shift = 24 - 8 * pass;
   __shared__ unsigned long long bins[256];
   const Ws w = ws_of(a);
   const int groups = (a.nqb + kRowsPerHist - 1) / kRowsPerHist;
@@ -253,8 +284,8 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
   if (pid < 0) return;                                       // uniform: the head is in no pool
   PoolState* ps = w.ps + pid;
   bins[threadIdx.x] = 0ull;
+  const uint32_t prefix = pool_prefix(a, ps, pass, threadIdx.x & 63);
   __syncthreads();
-  const uint32_t prefix = ps->prefix;
   const int i1 = min(i0 + kRowsPerHist, a.nqb);
   const int n = (i1 - i0) * a.nkb;                           // the rows' scores, contiguous
   const float* base = a.scores + ((int64_t)bh * a.nqb + i0) * a.nkb;
@@ -300,36 +331,7 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int shift) {
   if (acc) atomicAdd(&bins[cur], acc);
   __syncthreads();
   const unsigned long long v = bins[threadIdx.x];
-  if (v) atomicAdd(&ps->bins[threadIdx.x], v);
-}
-
-// Per pool: suffix sums of the bins (mass of digits >= d inside the current
-// prefix group); the digit is the largest d whose suffix reaches the
-// remaining target, and the mass of the larger digits leaves the target.  In
-// the first pass the bins hold the whole pool, so their sum is the pool's
-// mass and the target is ceil(p * mass).
-__global__ __launch_bounds__(kTpThreads) void tp_digit(TopPArgs a, int shift) {
-  __shared__ unsigned long long suf[257];
-  const Ws w = ws_of(a);
-  PoolState* ps = w.ps + blockIdx.x;
-  if (!ps->used) return;                                     // uniform
-  const int d = threadIdx.x;
-  suf[d] = ps->bins[d];
-  if (d == 0) suf[256] = 0ull;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {                        // suffix scan, integer: any order is exact
-    const unsigned long long v = d + o < 256 ? suf[d + o] : 0ull;
-    __syncthreads();
-    suf[d] += v;
-    __syncthreads();
-  }
-  const unsigned long long rem = shift == 24 ? (unsigned long long)ceil(a.top_p * (double)suf[0]) : ps->rem;
-  __syncthreads();                                           // every thread has read rem before it changes
-  if (suf[d] >= rem && suf[d + 1] < rem) {
-    ps->rem = rem - suf[d + 1];
-    ps->prefix |= (uint32_t)d << shift;
-  }
-  ps->bins[d] = 0ull;
+  if (v) atomicAdd(&ps->bins[pass][threadIdx.x], v);
 }
 
 // One row of tp_select with PER live slots per lane (64 * PER >= nkb).
@@ -371,17 +373,12 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
   auto key = [&](int mm) { return lane + 64 * mm < n ? okey(sc(mm)) : 0u; };
   uint32_t T;
   if (pooled) {
-    T = w.ps[pid].prefix;
+    T = pool_prefix(a, w.ps + pid, 4, lane);
   } else {
     // the row's own threshold: a radix select over its order keys, four
     // 8-bit digits, with integer bin masses in this wave's LDS bins (the
     // same search as the pooled domains')
-    unsigned long long tot = 0ull;
-#pragma unroll
-    for (int mm = 0; mm < PER; ++mm)
-      if (lane + 64 * mm < n) tot += fixed_mass(sc(mm));
-    tot = wave_sum_u64(tot);
-    unsigned long long rem = (unsigned long long)ceil(a.top_p * (double)tot);
+    unsigned long long rem = 0ull;
     T = 0u;
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
@@ -405,41 +402,11 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
       }
       if (acc) atomicAdd(&bins[cur], acc);
       wave_lds_sync();
-      // suffix sums: lane l holds digits 4l .. 4l + 3
+      // lane l holds digits 4l .. 4l + 3
       unsigned long long v[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) v[b] = bins[4 * lane + b];
-      v[2] += v[3];
-      v[1] += v[2];
-      v[0] += v[1];
-      unsigned long long above = 0ull;                       // digits of the lanes above
-      unsigned long long x = v[0];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_down(x, o, 64);
-        if (lane + o < 64) {
-          above += y;
-          x += y;
-        }
-      }
-      // x: suffix from digit 4l on; above: from digit 4l + 4 on
-      int dig = -1;
-      unsigned long long past = 0ull;
-#pragma unroll
-      for (int b = 3; b >= 0; --b) {
-        const unsigned long long sb = v[b] + above;                        // digits >= 4l + b
-        const unsigned long long sn = (b == 3 ? 0ull : v[b + 1]) + above;  // digits >= 4l + b + 1
-        if (dig < 0 && sb >= rem && sn < rem) {
-          dig = 4 * lane + b;
-          past = sn;
-        }
-      }
-      const uint64_t who = __ballot(dig >= 0);
-      const int src = (int)__builtin_ctzll(who);
-      dig = __shfl(dig, src, 64);
-      past = __shfl(past, src, 64);
-      rem -= past;
-      T |= (uint32_t)dig << shift;
+      T |= (uint32_t)wave_digit(v, rem, shift == 24, a.top_p, lane) << shift;
       wave_lds_sync();                                       // the bins are cleared next
     }
   }
@@ -522,10 +489,8 @@ hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
   if (a.domain != 0) {
     const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + kRowsPerHist - 1) / kRowsPerHist));
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, shift);
-      hipLaunchKernelGGL(tp_digit, dim3((unsigned)a.npools), dim3(kTpThreads), 0, stream, a, shift);
-    }
+    for (int pass = 0; pass < 4; ++pass)
+      hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, pass);
   }
   const int per = (a.nkb + 63) / 64;
   if (per <= 1) hipLaunchKernelGGL(tp_select<1>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
