@@ -139,6 +139,29 @@ __device__ void value_norms(const TopPArgs& a, const Ws& w, int g) {
   }
 }
 
+// Natural log of a positive normal double.  x = 2^e m with m in
+// [sqrt(1/2), sqrt(2)); log m = 2 atanh(f) with f = (m - 1) / (m + 1), summed
+// as its odd power series 2 (f + f^3/3 + f^5/5 + ...) -- |f| <= 0.172, so
+// eleven terms reach double precision -- and e ln 2 is added in two parts
+// (ln 2 to 32 significant bits, exact when multiplied by e, and the rest).
+// Within a few ulps of the correctly rounded log.
+__device__ __forceinline__ double log_pos(double x) {
+  int e;
+  double m = frexp(x, &e);                                   // m in [1/2, 1)
+  if (m < 0.70710678118654752440) {
+    m *= 2.0;
+    e -= 1;
+  }
+  const double f = (m - 1.0) / (m + 1.0);
+  const double f2 = f * f;
+  double p = 2.0 / 21.0;
+#pragma unroll
+  for (int k = 9; k >= 0; --k) p = fma(p, f2, 2.0 / (double)(2 * k + 1));
+  constexpr double kLn2Hi = 0x1.62e42ff000000p-1, kLn2Lo = -0x1.718432a1b0e26p-35;
+  const double ed = (double)e;
+  return fma(ed, kLn2Hi, fma(ed, kLn2Lo, f * p));
+}
+
 // one wave per row; workgroups from ent_groups on compute value norms
 __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a, int ent_groups) {
   const Ws w = ws_of(a);
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(kTpThreads) void tp_row_entropy(TopPArgs a, int ent
   double acc = 0.0;
   for (int j = lane; j < a.nkb; j += 64) {
     const double p = (double)s[j];
-    acc -= p * log(p + eps);
+    acc -= p * log_pos(p + eps);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -342,12 +365,29 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// The row's scores stay in registers (PER < 16) or in this wave's LDS
-// (srow, slot mm of lane l at mm * 64 + l): only the lane that wrote a slot
+// floor(s * 2^32) + 1 for the score s >= 0 of an order key, in integers
+// (the same value as fixed_mass: s = m * 2^(E - 150) with a 24-bit m)
+__device__ __forceinline__ unsigned long long mass_of_key(uint32_t k) {
+  const uint32_t u = k & 0x7fffffffu;                        // s >= 0: the key is u | 2^31
+  const int E = (int)(u >> 23);
+  if (E == 0) return 1ull;                                   // zero or subnormal
+  const unsigned long long m = (unsigned long long)((u & 0x7fffffu) | 0x800000u);
+  const int sh = E - 118;                                    // s * 2^32 = m * 2^sh
+  if (sh >= 0) return sh <= 40 ? (m << sh) + 1ull : fixed_mass(__uint_as_float(u));
+  return (sh > -24 ? (m >> (-sh)) : 0ull) + 1ull;
+}
+
+// the score of an order key
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The row's order keys stay in registers (PER < 16) or in this wave's LDS
+// (krow, slot mm of lane l at mm * 64 + l): only the lane that wrote a slot
 // reads it, so the LDS copy needs no synchronization.
 template <int PER>
 __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, int i, int lane,
-                           unsigned long long* bins, float* srow) {
+                           unsigned long long* bins, uint32_t* krow) {
   constexpr bool kLds = PER >= 16;
   const int n = a.nkb;
   const int pid = w.pool[bh];
@@ -357,48 +397,73 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
   int32_t* irow = a.idx + row * n;
   const bool dense = a.frame0_first >= 0 && i >= a.frame0_first && i <= a.frame0_last;
 
-  float sreg[kLds ? 1 : PER];
+  // order key of every slot; 0 (below every score's key) past the row.  The
+  // loads are issued together (slots past the row read the row's last block)
+  uint32_t kreg[kLds ? 1 : PER];
+  uint32_t inrow = 0u;                                       // slots inside the row
+  {
+    const float* srow_g = a.scores + row * n;
+    float sv[PER];
 #pragma unroll
-  for (int mm = 0; mm < PER; ++mm) {
-    const int j = lane + 64 * mm;
-    const float v = j < n ? score_of(a, w, bh, row, j, pooled) : 0.0f;
-    if constexpr (kLds) srow[mm * 64 + lane] = v;
-    else sreg[mm] = v;
+    for (int mm = 0; mm < PER; ++mm) sv[mm] = srow_g[min(lane + 64 * mm, n - 1)];
+    if (pooled && a.value_aware) {
+      const float* vn = w.vnorm + (int64_t)bh * a.vstride;
+#pragma unroll
+      for (int mm = 0; mm < PER; ++mm) sv[mm] = __fmul_rn(sv[mm], vn[min(lane + 64 * mm, n - 1)]);
+    }
+#pragma unroll
+    for (int mm = 0; mm < PER; ++mm) {
+      const bool in = lane + 64 * mm < n;
+      const uint32_t k = in ? okey(sv[mm]) : 0u;
+      inrow |= in ? 1u << mm : 0u;
+      if constexpr (kLds) krow[mm * 64 + lane] = k;
+      else kreg[mm] = k;
+    }
   }
-  auto sc = [&](int mm) -> float {
-    if constexpr (kLds) return srow[mm * 64 + lane];
-    else return sreg[mm];
+  auto key = [&](int mm) -> uint32_t {
+    if constexpr (kLds) return krow[mm * 64 + lane];
+    else return kreg[mm];
   };
-  // order key of slot mm; 0 (below every score's key) past the row
-  auto key = [&](int mm) { return lane + 64 * mm < n ? okey(sc(mm)) : 0u; };
   uint32_t T;
   if (pooled) {
     T = pool_prefix(a, w.ps + pid, 4, lane);
   } else {
     // the row's own threshold: a radix select over its order keys, four
     // 8-bit digits, with integer bin masses in this wave's LDS bins (the
-    // same search as the pooled domains')
+    // same search as the pooled domains').  Pass p visits only the slots
+    // that matched the digits of pass p - 1.
     unsigned long long rem = 0ull;
     T = 0u;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    uint32_t cand = inrow;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
 #pragma unroll
       for (int b = 0; b < 4; ++b) bins[4 * lane + b] = 0ull;
       wave_lds_sync();
       // a lane adds up a run of equal digits itself and makes one atomic per run
-      uint32_t cur = 256u;
+      uint32_t cur = 256u, next = 0u;
       unsigned long long acc = 0ull;
-#pragma unroll
-      for (int mm = 0; mm < PER; ++mm) {
-        const bool match = lane + 64 * mm < n && (shift == 24 || ((key(mm) ^ T) >> (shift + 8)) == 0u);
-        if (match) {
-          const uint32_t b = (key(mm) >> shift) & 255u;
+      auto visit = [&](int mm, uint32_t k) {
+        if (pass == 0 || ((k ^ T) >> (shift + 8)) == 0u) {
+          next |= 1u << mm;
+          const uint32_t b = (k >> shift) & 255u;
           if (b != cur) {
             if (acc) atomicAdd(&bins[cur], acc);
             cur = b;
             acc = 0ull;
           }
-          acc += fixed_mass(sc(mm));
+          acc += mass_of_key(k);
         }
+      };
+      if constexpr (kLds) {
+        for (uint32_t m = cand; m != 0u; m &= m - 1u) {
+          const int mm = __builtin_ctz(m);
+          visit(mm, krow[mm * 64 + lane]);
+        }
+      } else {
+#pragma unroll
+        for (int mm = 0; mm < PER; ++mm)
+          if ((cand >> mm) & 1u) visit(mm, kreg[mm]);
       }
       if (acc) atomicAdd(&bins[cur], acc);
       wave_lds_sync();
@@ -406,14 +471,15 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
       unsigned long long v[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) v[b] = bins[4 * lane + b];
-      T |= (uint32_t)wave_digit(v, rem, shift == 24, a.top_p, lane) << shift;
+      T |= (uint32_t)wave_digit(v, rem, pass == 0, a.top_p, lane) << shift;
+      cand = next;
       wave_lds_sync();                                       // the bins are cleared next
     }
   }
   // kept: score >= T; a pooled row left empty keeps its first largest block
   bool any = false;
 #pragma unroll
-  for (int mm = 0; mm < PER; ++mm) any = any || (lane + 64 * mm < n && key(mm) >= T);
+  for (int mm = 0; mm < PER; ++mm) any = any || (((inrow >> mm) & 1u) && key(mm) >= T);
   const bool row_empty = !__any(any);
   int safe = -1;
   if (pooled && row_empty) {
@@ -422,8 +488,9 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
 #pragma unroll
     for (int mm = 0; mm < PER; ++mm) {
       const int j = lane + 64 * mm;
-      if (j < n && (sc(mm) > best || (sc(mm) == best && j < bj))) {
-        best = sc(mm);
+      const float sv = key_score(key(mm));
+      if (j < n && (sv > best || (sv == best && j < bj))) {
+        best = sv;
         bj = j;
       }
     }
@@ -453,13 +520,10 @@ __device__ void select_row(const TopPArgs& a, const Ws& w, int bh, int64_t row, 
   }
   if (lane == 0) a.cnt[row] = run;
 }
-
-// PER: slots per lane, 64 * PER >= nkb (a kernel per PER, so each gets its
-// own register allocation)
 template <int PER>
 __global__ __launch_bounds__(kTpThreads) void tp_select(TopPArgs a) {
   __shared__ unsigned long long sel_bins[256 * (kTpThreads / 64)];
-  __shared__ float sel_rows[PER >= 16 ? 64 * PER * (kTpThreads / 64) : 1];
+  __shared__ uint32_t sel_rows[PER >= 16 ? 64 * PER * (kTpThreads / 64) : 1];
   const Ws w = ws_of(a);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kTpThreads / 64) + (threadIdx.x >> 6);
