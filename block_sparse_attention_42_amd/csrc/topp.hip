@@ -24,7 +24,7 @@
 //   tp_pools          one workgroup per batch element: median split, pool of
 //                     every head, pool state cleared
 //   tp_hist (x4)      radix passes of the pooled thresholds: integer bin
-//                     masses of kRowsPerHist rows per workgroup, each pass
+//                     masses of a few rows per workgroup, each pass
 //                     into its own bins; a pass starts by deriving the digits
 //                     of the passes before it from their bins (every wave, the
 //                     same suffix scans), and the first pass's bins add up to
@@ -32,6 +32,7 @@
 //   tp_select         one wave per row: threshold (the pool's, derived from
 //                     its four bin sets, or the row's own radix select),
 //                     safeguard, frame-0 rows, text columns, compaction
+#include <algorithm>
 #include <type_traits>
 
 #include "bsa_internal.h"
@@ -41,7 +42,8 @@ namespace {
 
 constexpr int kTpThreads = 256;
 constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks in registers
-constexpr int kRowsPerHist = 8;    // rows of one head per histogram workgroup
+constexpr int kMinHistRows = 8;    // rows of one head per histogram workgroup, at least
+constexpr int kHistGroupsPerPool = 512;   // about this many workgroups add to one pool's bins
 constexpr int kBatch = 8;          // loads a thread issues before it uses them
 constexpr int kNormRows = 16;      // pooled value rows per norm workgroup
 constexpr int kMaxHeads = 4096;    // heads of a batch element (head entropies in LDS)
@@ -285,60 +287,72 @@ __device__ __forceinline__ int wave_digit(unsigned long long (&v)[4], unsigned l
 // The order-key digits of a pool's threshold chosen by its first `passes`
 // radix passes (every wave that needs them derives them from the bins).
 __device__ __forceinline__ uint32_t pool_prefix(const TopPArgs& a, const PoolState* ps, int passes, int lane) {
+  unsigned long long v[4][4];                                // every pass's bins, loaded together
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[d][b] = d < passes ? ps->bins[d][4 * lane + b] : 0ull;
   uint32_t prefix = 0u;
   unsigned long long rem = 0ull;
-  for (int d = 0; d < passes; ++d) {
-    unsigned long long v[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) v[b] = ps->bins[d][4 * lane + b];
-    prefix |= (uint32_t)wave_digit(v, rem, d == 0, a.top_p, lane) << (24 - 8 * d);
-  }
+  for (int d = 0; d < 4; ++d)
+    if (d < passes) prefix |= (uint32_t)wave_digit(v[d], rem, d == 0, a.top_p, lane) << (24 - 8 * d);
   return prefix;
 }
 
-__global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int pass) {
+__global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int pass, int rows) {
   const int shift = 24 - 8 * pass;
   __shared__ unsigned long long bins[256];
   const Ws w = ws_of(a);
-  const int groups = (a.nqb + kRowsPerHist - 1) / kRowsPerHist;
+  const int groups = (a.nqb + rows - 1) / rows;
   const int bh = blockIdx.x / groups;
-  const int i0 = (blockIdx.x % groups) * kRowsPerHist;
+  const int i0 = (blockIdx.x % groups) * rows;
   const int pid = w.pool[bh];
   if (pid < 0) return;                                       // uniform: the head is in no pool
   PoolState* ps = w.ps + pid;
-  bins[threadIdx.x] = 0ull;
-  const uint32_t prefix = pool_prefix(a, ps, pass, threadIdx.x & 63);
-  __syncthreads();
-  const int i1 = min(i0 + kRowsPerHist, a.nqb);
+  const int t = threadIdx.x;
+  const int i1 = min(i0 + rows, a.nqb);
   const int n = (i1 - i0) * a.nkb;                           // the rows' scores, contiguous
   const float* base = a.scores + ((int64_t)bh * a.nqb + i0) * a.nkb;
   const float* vn = w.vnorm + (int64_t)bh * a.vstride;
+  // loads of a batch (elements past the rows read the last one and are
+  // skipped): scores and, for value-aware scores, the key blocks' norms
+  auto load = [&](int e0, float (&sv)[kBatch], float (&vv)[kBatch]) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) sv[u] = base[min(e0 + kTpThreads * u + t, n - 1)];
+    if (a.value_aware) {
+      int j = (e0 + t) % a.nkb;                              // key block of element u
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        vv[u] = vn[j];
+        j += kTpThreads;
+        while (j >= a.nkb) j -= a.nkb;
+      }
+    }
+  };
+  float sv[kBatch], vv[kBatch];
+  load(0, sv, vv);                                           // in flight while the digits are derived
+  bins[t] = 0ull;
+  const uint32_t prefix = pool_prefix(a, ps, pass, t & 63);
+  __syncthreads();
   // most scores share their leading digits: a thread adds up a run of equal
   // digits itself and makes one LDS atomic per run (integer sums: exact in
   // any order)
   uint32_t cur = 256u;
   unsigned long long acc = 0ull;
   for (int e0 = 0; e0 < n; e0 += kTpThreads * kBatch) {
-    float sv[kBatch];
+    float cs[kBatch], cv[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int e = e0 + kTpThreads * u + (int)threadIdx.x;
-      sv[u] = e < n ? base[e] : 0.0f;
+      cs[u] = sv[u];
+      cv[u] = vv[u];
     }
-    if (a.value_aware) {
-      int j = (e0 + (int)threadIdx.x) % a.nkb;              // key block of element u
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int e = e0 + kTpThreads * u + (int)threadIdx.x;
-        if (e < n) sv[u] = __fmul_rn(sv[u], vn[j]);
-        j += kTpThreads;
-        while (j >= a.nkb) j -= a.nkb;
-      }
-    }
+    if (e0 + kTpThreads * kBatch < n) load(e0 + kTpThreads * kBatch, sv, vv);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int e = e0 + kTpThreads * u + (int)threadIdx.x;
-      const uint32_t k = okey(sv[u]);
+      const int e = e0 + kTpThreads * u + t;
+      const float x = a.value_aware ? __fmul_rn(cs[u], cv[u]) : cs[u];
+      const uint32_t k = okey(x);
       const bool match = e < n && (shift == 24 || ((k ^ prefix) >> (shift + 8)) == 0u);
       if (match) {
         const uint32_t b = (k >> shift) & 255u;
@@ -347,14 +361,14 @@ __global__ __launch_bounds__(kTpThreads) void tp_hist(TopPArgs a, int pass) {
           cur = b;
           acc = 0ull;
         }
-        acc += fixed_mass(sv[u]);
+        acc += fixed_mass(x);
       }
     }
   }
   if (acc) atomicAdd(&bins[cur], acc);
   __syncthreads();
-  const unsigned long long v = bins[threadIdx.x];
-  if (v) atomicAdd(&ps->bins[pass][threadIdx.x], v);
+  const unsigned long long v = bins[t];
+  if (v) atomicAdd(&ps->bins[pass][t], v);
 }
 
 // One row of tp_select with PER live slots per lane (64 * PER >= nkb).
@@ -552,9 +566,14 @@ hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(tp_head_entropy, dim3((unsigned)a.BH), dim3(kTpThreads), 0, stream, a);
   hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
   if (a.domain != 0) {
-    const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + kRowsPerHist - 1) / kRowsPerHist));
+    // every workgroup of a pool adds its bins to the pool's with global
+    // atomics: more rows per workgroup when a pool spans many heads
+    const int64_t heads = a.domain == 1 ? 1 : a.domain == 3 ? a.H : (a.H + 1) / 2;
+    const int rows = (int)std::min<int64_t>(
+        a.nqb, std::max<int64_t>(kMinHistRows, (heads * a.nqb + kHistGroupsPerPool - 1) / kHistGroupsPerPool));
+    const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + rows - 1) / rows));
     for (int pass = 0; pass < 4; ++pass)
-      hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, pass);
+      hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, pass, rows);
   }
   const int per = (a.nkb + 63) / 64;
   if (per <= 1) hipLaunchKernelGGL(tp_select<1>, dim3(wave_groups), dim3(kTpThreads), 0, stream, a);
