@@ -45,17 +45,6 @@ constexpr int kImpRows = 16;    // centroid rows of a workgroup
 constexpr int kImpZMax = 16384; // logits of a workgroup (G * C * nkb)
 constexpr int kImpPrefetch = 64 * 128 / kImpThreads;   // token elements per thread (q_block * D <= 8192)
 
-template <typename T>
-__device__ __forceinline__ float widen(const T* p, int64_t e);
-template <>
-__device__ __forceinline__ float widen<bf16_t>(const bf16_t* p, int64_t e) {
-  return __uint_as_float((uint32_t)p[e].bits << 16);
-}
-template <>
-__device__ __forceinline__ float widen<float>(const float* p, int64_t e) {
-  return p[e];
-}
-
 // Sum of e_k = exp(z_k - mx) over a row of nkb logits by the halving tree
 // over the row padded to P (a power of two, P >= 2): level h adds k and
 // k + h for every k < h.  The first level computes the exponentials and
@@ -127,14 +116,19 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     return reinterpret_cast<const T*>(a.q) + ((int64_t)bh * a.seq_alloc + lo) * D;
   };
   auto block_n = [&](int g) { return (int)min((int64_t)a.q_block, a.S - (int64_t)(i0 + g) * a.q_block); };
-  float pre[kImpPrefetch];
+  // 16-byte chunks of a block's tokens, all of a thread's loads issued
+  // together (chunks past the block read its first chunk and are dropped)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kEpc = 16 / (int)sizeof(T);           // elements per chunk
+  constexpr int kChunks = kImpPrefetch / kEpc;        // chunks per thread
+  u32x4_t pre[kChunks];
   auto prefetch = [&](int g) {
-    const T* qb = block_tokens(g);
-    const int ne = block_n(g) * D;
+    const u32x4_t* qb = reinterpret_cast<const u32x4_t*>(block_tokens(g));
+    const int nc = block_n(g) * D / kEpc;
 #pragma unroll
-    for (int k = 0; k < kImpPrefetch; ++k) {
-      const int e = tid + k * kImpThreads;
-      pre[k] = e < ne ? widen(qb, e) : 0.0f;
+    for (int k = 0; k < kChunks; ++k) {
+      const int c = tid + k * kImpThreads;
+      pre[k] = qb[c < nc ? c : 0];
     }
   };
   prefetch(0);
@@ -143,9 +137,22 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     const int ce = min(C, n);
     float* mu = mu_all + g * C * D;
 #pragma unroll
-    for (int k = 0; k < kImpPrefetch; ++k) {
-      const int e = tid + k * kImpThreads;
-      if (e < n * D) xs[(e / D) * DP + e % D] = pre[k];
+    for (int k = 0; k < kChunks; ++k) {
+      const int e = (tid + k * kImpThreads) * kEpc;   // first element of the chunk
+      if (e < n * D) {
+        float* dst = xs + (e / D) * DP + e % D;       // kEpc consecutive channels of one token
+        if constexpr (sizeof(T) == 2) {
+          const u32x4_t w = pre[k];
+          *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                                        __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                                            __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+        } else {
+          const u32x4_t w = pre[k];
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3]));
+        }
+      }
     }
     if (g + 1 < nblk) prefetch(g + 1);
     __syncthreads();
