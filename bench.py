@@ -200,9 +200,10 @@ def top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, reps=20):
     """EG-Sparse routing (low-entropy heads pooled with value-aware scores, the
     rest per-row local), top-p 0.9, on P' of the same inputs (one cluster).
 
-    Not part of the timed step.  Algorithmic bytes: the scores are read by the
-    entropy, total, four radix and selection passes (7 reads of B*H*nqb*nkb
-    floats) and the mask, counts and lists written once.
+    Not part of the timed step.  Bytes counted: the scores read by the
+    entropy and the selection passes (every head) and by the four radix
+    passes (the pooled floor(H/2) heads), the pooled value rows read once for
+    their norms, and the mask, counts and lists written once.
     """
     import ctypes
     import numpy as np
@@ -228,7 +229,8 @@ def top_p_timing(bsa, w, g, qd, kd, vd, kp, nqb, nkb, stream, ev, reps=20):
     ms = float(np.median([e[0].elapsed_time(e[1]) for e in ts]))
     n = w.B * w.H * nqb * nkb
     kept = int(cnt.sum().item())
-    byts = 7.0 * n * 4 + n + 4.0 * kept + w.B * w.H * nqb * 4
+    pooled = (w.H // 2) / w.H
+    byts = (2.0 + 4.0 * pooled) * n * 4 + w.B * w.H * nkb * w.D * 4 + n + 4.0 * kept + w.B * w.H * nqb * 4
     gbs = byts / (ms * 1e-3) / 1e9
     return {"domain": "eg", "value_aware": True, "top_p": 0.9, "select_ms": round(ms, 4),
             "executed_blocks": kept,
