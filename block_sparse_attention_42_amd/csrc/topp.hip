@@ -43,7 +43,6 @@ namespace {
 constexpr int kTpThreads = 256;
 constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks in registers
 constexpr int kMinHistRows = 8;    // rows of one head per histogram workgroup, at least
-constexpr int kHistGroupsPerPool = 512;   // about this many workgroups add to one pool's bins
 constexpr int kBatch = 8;          // loads a thread issues before it uses them
 constexpr int kNormRows = 16;      // pooled value rows per norm workgroup
 constexpr int kMaxHeads = 4096;    // heads of a batch element (head entropies in LDS)
@@ -567,10 +566,12 @@ hipError_t launch_topp(const TopPArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(tp_pools, dim3((unsigned)a.B), dim3(kTpThreads), 0, stream, a);
   if (a.domain != 0) {
     // every workgroup of a pool adds its bins to the pool's with global
-    // atomics: more rows per workgroup when a pool spans many heads
+    // atomics, so a pool gets between 512 and 2048 workgroups: about one per
+    // 16 K scores (enough loads in flight for large pools, few atomics on the
+    // same bins for small ones)
     const int64_t heads = a.domain == 1 ? 1 : a.domain == 3 ? a.H : (a.H + 1) / 2;
-    const int rows = (int)std::min<int64_t>(
-        a.nqb, std::max<int64_t>(kMinHistRows, (heads * a.nqb + kHistGroupsPerPool - 1) / kHistGroupsPerPool));
+    const int64_t groups = std::min<int64_t>(2048, std::max<int64_t>(512, heads * a.nqb * a.nkb / 16384));
+    const int rows = (int)std::min<int64_t>(a.nqb, std::max<int64_t>(kMinHistRows, (heads * a.nqb + groups - 1) / groups));
     const unsigned hist_groups = (unsigned)((int64_t)a.BH * ((a.nqb + rows - 1) / rows));
     for (int pass = 0; pass < 4; ++pass)
       hipLaunchKernelGGL(tp_hist, dim3(hist_groups), dim3(kTpThreads), 0, stream, a, pass, rows);
