@@ -44,6 +44,8 @@ constexpr int kImpWaves = kImpThreads / 64;
 constexpr int kImpRows = 16;    // centroid rows of a workgroup
 constexpr int kImpZMax = 16384; // logits of a workgroup (G * C * nkb)
 constexpr int kImpPrefetch = 64 * 128 / kImpThreads;   // token elements per thread (q_block * D <= 8192)
+constexpr int kMembWords = 1;   // 64-token words of a cluster's member set (q_block is 32 or 64)
+constexpr int kImpMaxC = 16;    // clusters per block (G * C <= 16)
 
 // Sum of e_k = exp(z_k - mx) over a row of nkb logits by the halving tree
 // over the row padded to P (a power of two, P >= 2): level h adds k and
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __shared__ int msz_all[kImpRows];                   // cluster sizes (0: empty or c >= C_eff)
   __shared__ int n_all[kImpRows];                     // valid tokens of each block
   __shared__ float zsum[kImpRows];                    // row sums of e
+  __shared__ uint64_t memb[kImpMaxC][kMembWords];     // tokens of each cluster of the current block
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int D = a.D;
@@ -101,8 +104,7 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   // area A: the tokens of one block during k-means, then the logit rows
   float* xs = lds;                                    // [q_block][D + 4]
   float* zs = lds;                                    // [G * C][nkb]
-  int* asg = reinterpret_cast<int*>(lds + a.area_a);  // [q_block]
-  float* dist = reinterpret_cast<float*>(asg + a.q_block);   // [C][q_block]
+  float* dist = lds + a.area_a + a.q_block;          // [C][q_block] (after q_block spare words)
 
   for (int e = tid; e < kImpRows * 128; e += kImpThreads) mu_all[e] = 0.0f;
   if (tid < kImpRows) msz_all[tid] = 0;
@@ -164,75 +166,90 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
     // distance of every (token, cluster) pair by its own thread, then the
     // nearest cluster of every token (lowest index among equals); with one
     // cluster every token is in it and no distance is needed
+    // The assignment leaves, per cluster, the bit set of its tokens (bit t:
+    // token t, n <= 64), written by ballot from the wave that took the tokens.
     auto assign = [&]() {
-      if (ce == 1) {
-        for (int t = tid; t < n; t += kImpThreads) asg[t] = 0;
-        __syncthreads();
-        return;
-      }
-      for (int e = tid; e < n * ce; e += kImpThreads) {
-        const int t = e % n, c = e / n;
-        const float* xr = xs + t * DP;
-        const float* mr = mu + c * D;
-        float acc = 0.0f;
+      if (ce > 1) {
+        for (int e = tid; e < n * ce; e += kImpThreads) {
+          const int t = e % n, c = e / n;
+          const float* xr = xs + t * DP;
+          const float* mr = mu + c * D;
+          float acc = 0.0f;
 #pragma unroll 4
-        for (int d = 0; d < D; d += 4) {
-          const float4 x4 = *reinterpret_cast<const float4*>(xr + d);
-          const float4 m4 = *reinterpret_cast<const float4*>(mr + d);
-          float df = __fsub_rn(x4.x, m4.x);
-          acc = __fadd_rn(acc, __fmul_rn(df, df));
-          df = __fsub_rn(x4.y, m4.y);
-          acc = __fadd_rn(acc, __fmul_rn(df, df));
-          df = __fsub_rn(x4.z, m4.z);
-          acc = __fadd_rn(acc, __fmul_rn(df, df));
-          df = __fsub_rn(x4.w, m4.w);
-          acc = __fadd_rn(acc, __fmul_rn(df, df));
-        }
-        dist[e] = acc;
-      }
-      __syncthreads();
-      for (int t = tid; t < n; t += kImpThreads) {
-        int best = 0;
-        float bd = dist[t];
-        for (int c = 1; c < ce; ++c) {
-          const float v = dist[c * n + t];
-          if (v < bd) {
-            bd = v;
-            best = c;
+          for (int d = 0; d < D; d += 4) {
+            const float4 x4 = *reinterpret_cast<const float4*>(xr + d);
+            const float4 m4 = *reinterpret_cast<const float4*>(mr + d);
+            float df = __fsub_rn(x4.x, m4.x);
+            acc = __fadd_rn(acc, __fmul_rn(df, df));
+            df = __fsub_rn(x4.y, m4.y);
+            acc = __fadd_rn(acc, __fmul_rn(df, df));
+            df = __fsub_rn(x4.z, m4.z);
+            acc = __fadd_rn(acc, __fmul_rn(df, df));
+            df = __fsub_rn(x4.w, m4.w);
+            acc = __fadd_rn(acc, __fmul_rn(df, df));
           }
+          dist[e] = acc;
         }
-        asg[t] = best;
+        __syncthreads();
+      }
+      if (wave < kMembWords) {                        // tokens 64 wave + lane: nearest cluster (lowest among equals)
+        const int t = tid;
+        int best = -1;
+        if (t < n) {
+          best = 0;
+          float bd = dist[t];
+          for (int c = 1; c < ce; ++c) {
+            const float v = dist[c * n + t];
+            if (v < bd) {
+              bd = v;
+              best = c;
+            }
+          }
+          if (ce == 1) best = 0;
+        }
+        for (int c = 0; c < ce; ++c) {
+          const uint64_t bits = __ballot(best == c);
+          if (lane == 0) memb[c][wave] = bits;
+        }
       }
       __syncthreads();
+    };
+    // the members of cluster c in ascending token order (wave-uniform c)
+    auto members = [&](int c, auto&& f) {
+#pragma unroll
+      for (int wd = 0; wd < kMembWords; ++wd) {
+        uint64_t m = memb[c][wd];
+        m = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(m >> 32)) << 32) |
+            (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)m);
+        while (m) {
+          const int t = 64 * wd + (int)__builtin_ctzll(m);
+          m &= m - 1;
+          f(t);
+        }
+      }
+    };
+    auto size_of = [&](int c) {
+      int m = 0;
+#pragma unroll
+      for (int wd = 0; wd < kMembWords; ++wd) m += __popcll(memb[c][wd]);
+      return m;
     };
     for (int it = 0; it < a.T; ++it) {
       assign();
       for (int e = tid; e < ce * D; e += kImpThreads) {
-        const int c = e / D, d = e % D;
-        // members in ascending token order; a non-member adds +0, which
-        // leaves a nonzero sum unchanged and can only turn a -0 sum into +0
-        // (the same distances and logits: both enter through x - mu and
-        // mu * k, and a zero logit is stored as +0)
+        const int c = e / D, d = e % D;                // c is the same across a wave (D is 64 or 128)
+        // the members' channel d in ascending token order
         float acc = 0.0f;
-        int m = 0;
-#pragma unroll 8
-        for (int t = 0; t < n; ++t) {
-          const bool in = asg[t] == c;
-          acc = __fadd_rn(acc, in ? xs[t * DP + d] : 0.0f);
-          m += in ? 1 : 0;
-        }
+        members(c, [&](int t) { acc = __fadd_rn(acc, xs[t * DP + d]); });
+        const int m = size_of(c);
         if (m > 0) mu[e] = __fdiv_rn(acc, (float)m);
       }
       __syncthreads();
     }
     assign();
-    if (tid < ce) {
-      int m = 0;
-      for (int t = 0; t < n; ++t) m += asg[t] == tid ? 1 : 0;
-      msz_all[g * C + tid] = m;
-    }
+    if (tid < ce) msz_all[g * C + tid] = size_of(tid);
     if (tid == 0) n_all[g] = n;
-    __syncthreads();                                  // xs and asg are reused by the next block
+    __syncthreads();                                  // xs and the member sets are reused by the next block
   }
 
   // ---- 2. logits of every centroid row against every key-block summary ----
