@@ -82,6 +82,77 @@ __device__ float row_tree_sum(float* zr, int nkb, int P, float mx, int lane) {
   return __shfl(v, 0, 64);
 }
 
+// Logits of the group's centroid rows (kImpRows, zero rows unused) against
+// the key-block summaries: a thread owns all rows x JT key blocks, each logit
+// a sequential non-fused chain over the D channels in ascending order.  The
+// summaries stream through a ring of registers PF chunks ahead; the
+// centroid chunks are LDS broadcasts at compile-time offsets.
+template <int JT, int D>
+__device__ __forceinline__ void centroid_logits(const ImpArgs& a, const float* kbase, const float* mu_all, float* zs,
+                                                int nkb, int R, int tid) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int NC = D / 4;
+  constexpr int PF = JT >= 4 ? 1 : 8 / JT;         // chunks ahead (JT = 4: the registers of 64 chains)
+  for (int base = 0; base < nkb; base += kImpThreads * JT) {
+    float acc[kImpRows][JT];
+    const f32x4_t* kr[JT];
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = min(base + tid + jj * kImpThreads, nkb - 1);
+      kr[jj] = reinterpret_cast<const f32x4_t*>(kbase + (int64_t)j * D);
+#pragma unroll
+      for (int r = 0; r < kImpRows; ++r) acc[r][jj] = 0.0f;
+    }
+    f32x4_t ring[PF][JT];
+#pragma unroll
+    for (int c = 0; c < PF; ++c)
+#pragma unroll
+      for (int jj = 0; jj < JT; ++jj) ring[c][jj] = kr[jj][c];
+#pragma nounroll
+    for (int c0 = 0; c0 < NC; c0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int c = c0 + u;
+        f32x4_t kv[JT];
+#pragma unroll
+        for (int jj = 0; jj < JT; ++jj) {
+          kv[jj] = ring[u][jj];
+          ring[u][jj] = kr[jj][min(c + PF, NC - 1)];   // past the row's end: a harmless reread
+        }
+#pragma unroll
+        for (int r = 0; r < kImpRows; ++r) {
+          const f32x4_t m = *reinterpret_cast<const f32x4_t*>(mu_all + r * D + 4 * c);
+#pragma unroll
+          for (int jj = 0; jj < JT; ++jj) {
+            float t = acc[r][jj];
+            t = __fadd_rn(t, __fmul_rn(m[0], kv[jj][0]));
+            t = __fadd_rn(t, __fmul_rn(m[1], kv[jj][1]));
+            t = __fadd_rn(t, __fmul_rn(m[2], kv[jj][2]));
+            t = __fadd_rn(t, __fmul_rn(m[3], kv[jj][3]));
+            acc[r][jj] = t;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int j = base + tid + jj * kImpThreads;
+      if (j < nkb) {
+        const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
+#pragma unroll
+        for (int r = 0; r < kImpRows; ++r) {
+          if (r < R) {
+            float z = __fmul_rn(acc[r][jj], a.scale);
+            if (a.log_cluster) z = __fadd_rn(z, lc);
+            if (z == 0.0f) z = 0.0f;                  // -0 -> +0
+            zs[r * nkb + j] = z;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int JT>
 __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -254,51 +325,10 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
 
   // ---- 2. logits of every centroid row against every key-block summary ----
   const int R = nblk * C;
-  const float* kbase = a.kp + (int64_t)bh * nkb * D;
-  for (int base = 0; base < nkb; base += kImpThreads * JT) {
-    float acc[kImpRows][JT];
-    const float* kr[JT];
-#pragma unroll
-    for (int jj = 0; jj < JT; ++jj) {
-      const int j = min(base + tid + jj * kImpThreads, nkb - 1);
-      kr[jj] = kbase + (int64_t)j * D;
-#pragma unroll
-      for (int r = 0; r < kImpRows; ++r) acc[r][jj] = 0.0f;
-    }
-    for (int d = 0; d < D; d += 4) {
-      float4 kv[JT];
-#pragma unroll
-      for (int jj = 0; jj < JT; ++jj) kv[jj] = *reinterpret_cast<const float4*>(kr[jj] + d);
-#pragma unroll
-      for (int r = 0; r < kImpRows; ++r) {
-        const float4 m = *reinterpret_cast<const float4*>(mu_all + r * D + d);
-#pragma unroll
-        for (int jj = 0; jj < JT; ++jj) {
-          float t = acc[r][jj];
-          t = __fadd_rn(t, __fmul_rn(m.x, kv[jj].x));
-          t = __fadd_rn(t, __fmul_rn(m.y, kv[jj].y));
-          t = __fadd_rn(t, __fmul_rn(m.z, kv[jj].z));
-          t = __fadd_rn(t, __fmul_rn(m.w, kv[jj].w));
-          acc[r][jj] = t;
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < JT; ++jj) {
-      const int j = base + tid + jj * kImpThreads;
-      if (j < nkb) {
-        const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
-#pragma unroll
-        for (int r = 0; r < kImpRows; ++r) {
-          if (r < R) {
-            float z = __fmul_rn(acc[r][jj], a.scale);
-            if (a.log_cluster) z = __fadd_rn(z, lc);
-            if (z == 0.0f) z = 0.0f;                  // -0 -> +0
-            zs[r * nkb + j] = z;
-          }
-        }
-      }
-    }
+  {
+    const float* kbase = a.kp + (int64_t)bh * nkb * D;
+    if (D == 128) centroid_logits<JT, 128>(a, kbase, mu_all, zs, nkb, R, tid);
+    else centroid_logits<JT, 64>(a, kbase, mu_all, zs, nkb, R, tid);
   }
   __syncthreads();
 
