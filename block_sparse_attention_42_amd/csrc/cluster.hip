@@ -82,26 +82,26 @@ __device__ float row_tree_sum(float* zr, int nkb, int P, float mx, int lane) {
   return __shfl(v, 0, 64);
 }
 
-// Logits of the group's centroid rows (kImpRows, zero rows unused) against
+// Logits of the group's first RR centroid rows (zero rows unused) against
 // the key-block summaries: a thread owns all rows x JT key blocks, each logit
 // a sequential non-fused chain over the D channels in ascending order.  The
 // summaries stream through a ring of registers PF chunks ahead; the
 // centroid chunks are LDS broadcasts at compile-time offsets.
-template <int JT, int D>
+template <int JT, int D, int RR>
 __device__ __forceinline__ void centroid_logits(const ImpArgs& a, const float* kbase, const float* mu_all, float* zs,
                                                 int nkb, int R, int tid) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   constexpr int NC = D / 4;
-  constexpr int PF = JT >= 4 ? 1 : 8 / JT;         // chunks ahead (JT = 4: the registers of 64 chains)
+  constexpr int PF = RR * JT >= 64 ? 1 : 8 / JT;   // chunks ahead (64 chains: the registers are spent)
   for (int base = 0; base < nkb; base += kImpThreads * JT) {
-    float acc[kImpRows][JT];
+    float acc[RR][JT];
     const f32x4_t* kr[JT];
 #pragma unroll
     for (int jj = 0; jj < JT; ++jj) {
       const int j = min(base + tid + jj * kImpThreads, nkb - 1);
       kr[jj] = reinterpret_cast<const f32x4_t*>(kbase + (int64_t)j * D);
 #pragma unroll
-      for (int r = 0; r < kImpRows; ++r) acc[r][jj] = 0.0f;
+      for (int r = 0; r < RR; ++r) acc[r][jj] = 0.0f;
     }
     f32x4_t ring[PF][JT];
 #pragma unroll
@@ -120,7 +120,7 @@ __device__ __forceinline__ void centroid_logits(const ImpArgs& a, const float* k
           ring[u][jj] = kr[jj][min(c + PF, NC - 1)];   // past the row's end: a harmless reread
         }
 #pragma unroll
-        for (int r = 0; r < kImpRows; ++r) {
+        for (int r = 0; r < RR; ++r) {
           const f32x4_t m = *reinterpret_cast<const f32x4_t*>(mu_all + r * D + 4 * c);
 #pragma unroll
           for (int jj = 0; jj < JT; ++jj) {
@@ -140,7 +140,7 @@ __device__ __forceinline__ void centroid_logits(const ImpArgs& a, const float* k
       if (j < nkb) {
         const float lc = (j == nkb - 1) ? a.ln_last : a.ln_full;
 #pragma unroll
-        for (int r = 0; r < kImpRows; ++r) {
+        for (int r = 0; r < RR; ++r) {
           if (r < R) {
             float z = __fmul_rn(acc[r][jj], a.scale);
             if (a.log_cluster) z = __fadd_rn(z, lc);
@@ -327,8 +327,14 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   const int R = nblk * C;
   {
     const float* kbase = a.kp + (int64_t)bh * nkb * D;
-    if (D == 128) centroid_logits<JT, 128>(a, kbase, mu_all, zs, nkb, R, tid);
-    else centroid_logits<JT, 64>(a, kbase, mu_all, zs, nkb, R, tid);
+    // a group of at most 8 centroid rows (G = 2 at long rows) computes only those
+    if (a.G * C <= 8) {
+      if (D == 128) centroid_logits<JT, 128, 8>(a, kbase, mu_all, zs, nkb, R, tid);
+      else centroid_logits<JT, 64, 8>(a, kbase, mu_all, zs, nkb, R, tid);
+    } else {
+      if (D == 128) centroid_logits<JT, 128, kImpRows>(a, kbase, mu_all, zs, nkb, R, tid);
+      else centroid_logits<JT, 64, kImpRows>(a, kbase, mu_all, zs, nkb, R, tid);
+    }
   }
   __syncthreads();
 
