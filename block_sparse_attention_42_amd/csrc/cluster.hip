@@ -17,12 +17,14 @@
 //      (token, cluster) distance, a sequential non-fused chain over the
 //      channels; the lowest cluster among equals) and replaces every
 //      non-empty centroid by the mean of its tokens (one thread per
-//      (cluster, channel), ascending tokens); a final assignment gives the
-//      cluster sizes;
+//      (cluster, channel) walks the cluster's member set, a 64-bit ballot of
+//      the assignment, in ascending token order); a final assignment gives
+//      the cluster sizes;
 //   2. logits of every centroid of the group against every key-block summary
-//      (the same chain as the block logits of the mask): a thread owns all 16
-//      centroid rows x JT key blocks, so each summary read from L2 feeds 16
-//      chains and each centroid read is an LDS broadcast;
+//      (the same chain as the block logits of the mask): a thread owns all
+//      the group's centroid rows (8 or 16) x JT key blocks, so each summary
+//      read from L2 feeds that many chains and each centroid read is an LDS
+//      broadcast;
 //   3. per non-empty centroid row, one wave: row max, e = exp(z - max) by the
 //      fixed-order exponential, the sum by a halving tree over the row padded
 //      to a power of two (pairs k, k + h at every level; the levels of 64 and

@@ -17,9 +17,10 @@
 // wave's LDS.  Every block with score >= T is kept.
 //
 // Kernels, in launch order (grid-wide dependencies between them):
-//   tp_row_entropy    one wave per row: sum_j -P log(P + eps) (float64); the
-//                     workgroups past the rows take the norms of the pooled
-//                     value rows (value-aware scores)
+//   tp_row_entropy    one wave per row: sum_j -P log(P + eps) (float64, the
+//                     log by its own series); the workgroups past the rows
+//                     take the norms of the pooled value rows (value-aware
+//                     scores)
 //   tp_head_entropy   one workgroup per head: the mean over its rows
 //   tp_pools          one workgroup per batch element: median split, pool of
 //                     every head, pool state cleared
@@ -33,7 +34,6 @@
 //                     its four bin sets, or the row's own radix select),
 //                     safeguard, frame-0 rows, text columns, compaction
 #include <algorithm>
-#include <type_traits>
 
 #include "bsa_internal.h"
 
@@ -41,7 +41,7 @@ namespace bsa {
 namespace {
 
 constexpr int kTpThreads = 256;
-constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks in registers
+constexpr int kTpPerLane = 32;     // rows of up to 2048 key blocks: 32 slots a lane
 constexpr int kMinHistRows = 8;    // rows of one head per histogram workgroup, at least
 constexpr int kBatch = 8;          // loads a thread issues before it uses them
 constexpr int kNormRows = 16;      // pooled value rows per norm workgroup
