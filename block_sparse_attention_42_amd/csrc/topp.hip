@@ -83,12 +83,6 @@ __device__ __forceinline__ Ws ws_of(const TopPArgs& a) {
   return w;
 }
 
-// the ranking score of block j of a row of head bh
-__device__ __forceinline__ float score_of(const TopPArgs& a, const Ws& w, int bh, int64_t row, int j, bool pooled) {
-  const float s = a.scores[row * a.nkb + j];
-  return (a.value_aware && pooled) ? __fmul_rn(s, w.vnorm[(int64_t)bh * a.vstride + j]) : s;
-}
-
 // Correctly rounded square root of x >= 0.  The compiler's root may be the
 // hardware's approximate one; it is moved to the float whose rounding
 // interval holds sqrt(x), decided exactly in double: a midpoint of two
