@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
   __shared__ int n_all[kImpRows];                     // valid tokens of each block
   __shared__ float zsum[kImpRows];                    // row sums of e
   __shared__ uint64_t memb[kImpMaxC][kMembWords];     // tokens of each cluster of the current block
+  __shared__ uint64_t memb_prev[kImpMaxC][kMembWords];   // the same after the assignment before
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int D = a.D;
@@ -282,7 +283,10 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
         }
         for (int c = 0; c < ce; ++c) {
           const uint64_t bits = __ballot(best == c);
-          if (lane == 0) memb[c][wave] = bits;
+          if (lane == 0) {
+            memb_prev[c][wave] = memb[c][wave];
+            memb[c][wave] = bits;
+          }
         }
       }
       __syncthreads();
@@ -307,8 +311,22 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
       for (int wd = 0; wd < kMembWords; ++wd) m += __popcll(memb[c][wd]);
       return m;
     };
+    // Lloyd's rounds end early once an assignment repeats the one before it:
+    // the means of the same members are the same centroids, so every later
+    // round would repeat it too (and the final assignment is this one)
+    bool converged = false;
     for (int it = 0; it < a.T; ++it) {
       assign();
+      if (it > 0) {
+        bool same = true;                             // the same LDS words for every thread: uniform
+        for (int c = 0; c < ce; ++c)
+#pragma unroll
+          for (int wd = 0; wd < kMembWords; ++wd) same = same && memb[c][wd] == memb_prev[c][wd];
+        if (same) {
+          converged = true;
+          break;
+        }
+      }
       for (int e = tid; e < ce * D; e += kImpThreads) {
         const int c = e / D, d = e % D;                // c is the same across a wave (D is 64 or 128)
         // the members' channel d in ascending token order
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(kImpThreads) void importance_kernel(ImpArgs a) {
       }
       __syncthreads();
     }
-    assign();
+    if (!converged) assign();
     if (tid < ce) msz_all[g * C + tid] = size_of(tid);
     if (tid == 0) n_all[g] = n;
     __syncthreads();                                  // xs and the member sets are reused by the next block
