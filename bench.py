@@ -161,7 +161,9 @@ def cluster_selector_timing(bsa, w, g, p, qd, kp, C, T, nqb, nkb, stream, ev, re
 
     Not part of the timed step.  VALU work per query block (lane-ops):
     k-means (T+1) * n * C * D * 3 + T * n * C * D, logits C * nkb * D * 2;
-    the exponentials and the mixture are counted as C * nkb * 30.
+    the exponentials and the mixture are counted as C * nkb * 30.  The
+    k-means term counts all T rounds; the kernel stops once an assignment
+    repeats, so the rate is an effective one.
     """
     import numpy as np
     import torch
