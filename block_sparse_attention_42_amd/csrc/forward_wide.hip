@@ -16,11 +16,17 @@
 //   * the block's selected keys are walked in 64-key steps (two 32-key
 //     sub-tiles: one 64-key block, or two 32-key / four 16-key blocks
 //     gathered), so the per-step work that does not scale with keys (list
-//     entries, tile addressing, waits, the rescale test) is paid once per
+//     entries, tile addressing, waits) is paid once per
 //     64 MFMAs;
 //   * a step is four phases of 16 MFMAs: S^T(u+1) of each sub-tile (K Q^T),
 //     then O^T += V^T P^T(u) of each sub-tile.  The exponentials of S(u)
-//     run between the first three phases, the row max of S(u+1) in the last;
+//     run between the first three phases; on the tracked path (below) the
+//     row max of S(u+1) runs in the last;
+//   * the softmax reference is the first step's row max, kept for the whole
+//     row: no per-step row max and no rescale (about 44 vector instructions
+//     of a step's ~300).  A row sum that ends at or above 2^64 (or not
+//     finite) makes the block run again on the tracked path: the row max of
+//     every step and a lazy rescale whenever it grows by more than 8 (log2);
 //   * K and V fragments stream through one ring of registers, each read
 //     from LDS five fragments ahead of its first MFMA;
 //   * every phase issues the eight DMA loads (HBM/L2 -> LDS, no VGPR
@@ -301,15 +307,6 @@ void fwd_wide_kernel(FwdArgs a) {
   float m_run[QT], thr[QT];
   float lp[QT][4];                     // row sum in four independent parts
   f32x16 o[QT][DT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = -INFINITY;
-    thr[qt] = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lp[qt][i] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
-  }
 
   // Row max (log2 domain, scale and weights applied) of a step's scores:
   // the lane's 32 keys per query tile in four groups of 8 (sub-tile h,
@@ -378,6 +375,25 @@ void fwd_wide_kernel(FwdArgs a) {
 
   auto tile_wait = [&](auto n) { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(n)::value) : "memory"); };
 
+  // Pass 0 keeps the reference max at the first step's row max for the whole
+  // row: no per-step row max, no rescale.  Every p is then at most l, so a
+  // row sum l below 2^64 (and finite) bounds P (bf16), O and l (fp32) far
+  // from overflow for any 2^17 keys of |v| < 2^40, and the result is the
+  // softmax up to rounding (the reference cancels in O / l).  A block with a
+  // row outside that bound runs again as pass 1: the lazy rescale, with the
+  // row max of every step (the tracked path).
+#pragma nounroll
+  for (int pass = 0;; ++pass) {
+  const bool track = pass != 0;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    thr[qt] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lp[qt][i] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x16{};
+  }
   if (nsteps > 0) {
     f32x16 sc[2][2][QT];      // [buffer][sub-tile][query tile]: S of steps u (buffer u&1) and u+1
     bf16x8 ring[kRing];       // K / V fragments in flight
@@ -561,11 +577,13 @@ void fwd_wide_kernel(FwdArgs a) {
                            : s == 16 ? 6 : s == 18 ? 7 : s == 21 ? 8 : s == 24 ? 9 : s == 26 ? 10 : s == 29 ? 11
                            : s == 32 ? 12 : s == 35 ? 13 : s == 38 ? 14 : s == 41 ? 15 : -1;
         if constexpr (unit >= 0) pair(unit / 8, unit % 8);
-        // row max of S(u+1) over phase 3
-        if constexpr (s >= 48 && (s - 48) % 3 == 0 && (s - 48) / 3 < 5) rowmax_stage(snext, i_u1, pm, mx, (s - 48) / 3);
+        // row max of S(u+1) over phase 3, on the tracked path only
+        if constexpr (s >= 48 && (s - 48) % 3 == 0 && (s - 48) / 3 < 5) {
+          if (track) rowmax_stage(snext, i_u1, pm, mx, (s - 48) / 3);
+        }
       });
 
-      if (u + 1 < nsteps) {
+      if (track && u + 1 < nsteps) {
         bool grow = false;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) grow = grow || mx[qt] > thr[qt];
@@ -590,6 +608,15 @@ void fwd_wide_kernel(FwdArgs a) {
   fence_o();
   // the last steps' loads must land before the LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (track || nsteps == 0) break;
+  bool unbounded = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l = add_xor32((lp[qt][0] + lp[qt][1]) + (lp[qt][2] + lp[qt][3]));
+    unbounded = unbounded || !(l < 0x1p64f);
+  }
+  if (!__any(unbounded)) break;
+  }
 
   // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
   float* ostage = reinterpret_cast<float*>(k_lds0);

@@ -281,6 +281,43 @@ def test_forward_arbitrary_lists_weights_and_nan_pads():
     assert np.abs(out2.float().cpu().numpy()[0, 0, :o.shape[0]] - o).max() <= tolerances(w)[0]
 
 
+@pytest.mark.parametrize("bk", [16, 32, 64])
+def test_forward_row_max_far_above_the_first_step(bk):
+    """The 64-row forward keeps the first step's row max as the softmax
+    reference; a row whose later blocks score far higher (here log-weights of
+    +60 after a first step at 0: 2^86 times larger) runs again with the row max
+    of every step.  Both kinds of rows, and rows whose later blocks score far
+    lower (-60), agree with the oracle."""
+    w = tiny(text_len=7, frames=3, lh=8, lw=12, bq=64, bk=bk, D=128, H=2, dtype="bf16", align=64,
+             centroids=4, grid=(2, 2))
+    g = geometry_of(w)
+    q, k, v = inputs_of(w)
+    rng = np.random.default_rng(11)
+    ne = 64 // bk                                   # list entries of the first 64-key step
+    cnt = np.zeros((g.B, g.H, g.nqb), np.int32)
+    idx = np.full((g.B, g.H, g.nqb, g.nkb), -1, np.int32)
+    lw = np.zeros((g.B, g.H, g.nqb, g.nkb), np.float32)
+    for h in range(g.H):
+        for i in range(g.nqb):
+            c = int(rng.integers(ne + 1, g.nkb + 1))
+            js = np.sort(rng.choice(g.nkb, c, replace=False))
+            cnt[0, h, i] = c
+            idx[0, h, i, :c] = js
+            kind = (h * g.nqb + i) % 3
+            if kind == 0:
+                lw[0, h, i, ne + int(rng.integers(0, c - ne))] = 60.0     # past the bound: the row runs again
+            elif kind == 1:
+                lw[0, h, i, ne:c] = -60.0                                  # later blocks vanish
+    gg = _geo(w)
+    qd, kd, vd = _dev(w, q), _dev(w, k), _dev(w, v)
+    out, lse = bsa.bsa_forward(qd, kd, vd, gg, torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(lw).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item() and not torch.isinf(out).any().item()
+    r = dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+    _check_out(w, r, q, k, v, g, cnt, idx, lw, {(0, h): list(range(g.nqb)) for h in range(g.H)})
+
+
 # seq_alloc past the last query block: rows no query block covers must still
 # be written as 0 (LSE -inf), with and without the key split, by each kernel
 TAIL = {
