@@ -110,3 +110,41 @@ def test_split_of_one_is_the_plain_forward():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), a.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), la.view(torch.int32))
+
+
+@pytest.mark.parametrize("bk", [16, 64])
+def test_split_parts_past_the_reference_bound(bk):
+    """Each part of a split frame-0 row keeps its own first step's row max as
+    the softmax reference; parts whose later blocks score far higher (+60 in
+    log-weight) run again with the row max of every step, parts whose later
+    blocks score far lower (-60) do not, and the merged rows match the oracle."""
+    w = tiny(text_len=11, frames=4, lh=8, lw=16, bq=64, bk=bk, D=128, H=2, dtype="bf16", mode="topk",
+             topk=0, keep_ratio=0.3, centroids=8, grid=(2, 4), align=64)
+    g = geometry_of(w)
+    q, k, v = inputs_of(w)
+    gg = P._geo(w)
+    qd, kd, vd = P._dev(w, q), P._dev(w, k), P._dev(w, v)
+    _, cnt, idx, _ = bsa.bsa_build_mask(bsa.bsa_pool_blocks(qd, gg, gg.q_block),
+                                        bsa.bsa_pool_blocks(kd, gg, gg.k_block), gg, P._mp(w))
+    c, ix = cnt.cpu().numpy(), idx.cpu().numpy()
+    lw = np.zeros(ix.shape, np.float32)
+    rng = np.random.default_rng(3)
+    for h in range(g.H):
+        for i in range(g.nqb):
+            n = int(c[0, h, i])
+            if n < 4:
+                continue
+            if (h + i) % 2 == 0:
+                lw[0, h, i, int(rng.integers(n // 2, n))] = 60.0
+            else:
+                lw[0, h, i, n // 2:n] = -60.0
+    lwd = torch.from_numpy(lw).cuda()
+    for split in (1, 3):
+        P._say(f"[gpu] split bound bk={bk} x{split}")
+        out = torch.full_like(qd, float("nan"))
+        lse = torch.full((w.B, w.H, w.seq_alloc), float("nan"), device=qd.device)
+        out, lse = bsa.bsa_forward(qd, kd, vd, gg, cnt, idx, lwd, out=out, lse=lse, dense_split=split)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item() and not torch.isinf(out).any().item()
+        r = dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+        P._check_out(w, r, q, k, v, g, c, ix, lw, {(0, h): list(range(g.nqb)) for h in range(g.H)})
