@@ -619,43 +619,82 @@ void fwd_wide_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: normalize, LSE, rows out through LDS for coalesced stores ----
-  float* ostage = reinterpret_cast<float*>(k_lds0);
-  bf16_t* Ob = reinterpret_cast<bf16_t*>(a.out) + (int64_t)bh * a.seq_alloc * D;
   constexpr int QB = 64;
-  float* wsO = part_item ? a.ws + (int64_t)blockIdx.x * QB * D : nullptr;
-  float* wsM = part_item ? a.ws + (int64_t)a.n_dense * QB * D + (int64_t)blockIdx.x * QB : nullptr;
-  float* wsL = part_item ? wsM + (int64_t)a.n_dense * QB : nullptr;
-  constexpr int C8 = D / 8;
+  constexpr int C8 = D / 8;            // 16-byte chunks of a bf16 row, 8 floats of a float row
+  if (!part_item) {
+    // A query tile's 32 rows of bf16 O (256 B each) fill K slot 0.  The lane
+    // of query qc and half hf holds d = 8ch + 4hf + 0..3 of each 16-byte chunk
+    // ch of its row.  Chunks are XOR-swizzled by the row, and in rows 16..31
+    // the two 8-byte halves of a chunk trade places, so each half-wave's
+    // writes and each quarter-wave's reads (one row) cover all banks once.
+    uint8_t* stage = reinterpret_cast<uint8_t*>(k_lds0);
+    bf16_t* Ob = reinterpret_cast<bf16_t*>(a.out) + (int64_t)bh * a.seq_alloc * D;
+    const uint32_t hb = 8u * (uint32_t)(hf ^ (qc >> 4));
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float l = add_xor32((lp[qt][0] + lp[qt][1]) + (lp[qt][2] + lp[qt][3]));
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const int64_t qrow0 = q0 + 32 * qt;
+      if (hf == 0 && a.lse) {
+        const int64_t row = qrow0 + qc;
+        const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
+        if (row < a.seq_alloc)
+          a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
+      }
+      // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x16 t = o[qt][dt];
+        asm volatile("" : "+v"(t));   // one tile in vector registers at a time
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ch = 4 * dt + r4;
+          const uint32_t off = (uint32_t)qc * (uint32_t)(D * 2) + (uint32_t)((ch ^ (qc & 15)) * 16) + hb;
+          *reinterpret_cast<uint2*>(stage + off) =
+              make_uint2(pack_bf16x2(t[4 * r4] * inv, t[4 * r4 + 1] * inv),
+                         pack_bf16x2(t[4 * r4 + 2] * inv, t[4 * r4 + 3] * inv));
+        }
+      }
+      // 4 rows per pass, a quarter-wave per row: 1 KB of contiguous rows per store
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rl = 4 * it + (lane >> 4), j = lane & 15;
+        const int64_t row = qrow0 + rl;
+        uint4 x = *reinterpret_cast<const uint4*>(stage + rl * (D * 2) + ((j ^ (rl & 15)) * 16));
+        if (it >= 4) x = make_uint4(x.z, x.w, x.x, x.y);
+        if (row >= a.S) x = make_uint4(0u, 0u, 0u, 0u);
+        if (row < a.seq_alloc) *reinterpret_cast<uint4*>(Ob + row * D + j * 8) = x;
+      }
+    }
+    return;
+  }
+  // a part of a split frame-0 row: unnormalized O (float), row max and row sum
+  float* ostage = reinterpret_cast<float*>(k_lds0);
+  float* wsO = a.ws + (int64_t)blockIdx.x * QB * D;
+  float* wsM = a.ws + (int64_t)a.n_dense * QB * D + (int64_t)blockIdx.x * QB;
+  float* wsL = wsM + (int64_t)a.n_dense * QB;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float l = add_xor32((lp[qt][0] + lp[qt][1]) + (lp[qt][2] + lp[qt][3]));
-    const float inv = part_item ? 1.0f : (l > 0.0f ? 1.0f / l : 0.0f);
     const int64_t qrow0 = q0 + 32 * qt;
-    if (part_item) {
-      if (hf == 0) {
-        wsM[32 * qt + qc] = m_run[qt];
-        wsL[32 * qt + qc] = l;
-      }
-    } else if (hf == 0 && a.lse) {
-      const int64_t row = qrow0 + qc;
-      const float mu = m_run[qt] == -INFINITY ? 0.0f : m_run[qt];
-      if (row < a.seq_alloc)
-        a.lse[(int64_t)bh * a.seq_alloc + row] = (row < a.S && l > 0.0f) ? (mu + __log2f(l)) * kLn2 : -INFINITY;
+    if (hf == 0) {
+      wsM[32 * qt + qc] = m_run[qt];
+      wsL[32 * qt + qc] = l;
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // O^T register r of d tile dt is d = 32dt + 8(r/4) + 4hf + r%4 of query qc
+      // 16 rows of floats per pass
       if ((qc >> 4) == half) {
         const int q = qc & 15;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           f32x16 t = o[qt][dt];
-          asm volatile("" : "+v"(t));   // one tile in vector registers at a time
+          asm volatile("" : "+v"(t));
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int ch = 8 * dt + 2 * r4 + hf;
             *reinterpret_cast<f32x4*>(ostage + q * D + ((ch ^ q) * 4)) =
-                f32x4{t[4 * r4], t[4 * r4 + 1], t[4 * r4 + 2], t[4 * r4 + 3]} * inv;
+                f32x4{t[4 * r4], t[4 * r4 + 1], t[4 * r4 + 2], t[4 * r4 + 3]};
           }
         }
       }
@@ -673,8 +712,7 @@ void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
           for (int c = 0; c < 8; ++c) v[c] = 0.0f;
         }
-        if (part_item) store8<float>(wsO + (row - q0) * D + c8 * 8, v);
-        else store8<bf16_t>(Ob + row * D + c8 * 8, v);
+        store8<float>(wsO + (row - q0) * D + c8 * 8, v);
       }
     }
   }
