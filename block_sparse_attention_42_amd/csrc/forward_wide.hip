@@ -34,7 +34,9 @@
 //     finished reading, so each tile has about two phases to land;
 //   * row sums go to four independent accumulators per query tile, so the
 //     v_dot2 chain never waits on itself; row maxima use v_max3 throughout
-//     (scores are finite or -inf, so no NaN canonicalization is needed).
+//     (scores are finite or -inf, so no NaN canonicalization is needed);
+//   * the epilogue rounds O to bf16 before staging it in LDS, a whole query
+//     tile (32 rows) per pass, so no lane sits out half of the staging.
 #include "fwd_common.h"
 
 namespace bsa {
