@@ -25,13 +25,21 @@ bsa = pytest.importorskip("block_sparse_attention_42_amd")
 MAX_ABS, MEAN_ABS = 2e-2, 2e-3          # bf16 inputs: bf16 products, float32 accumulation
 
 
+# bf16 LSE, absolute part: the row sum adds the same bf16-rounded P that the
+# P.V product uses (so O / l stays consistent).  Each p is within half a bf16
+# ulp, 2^-8 relative, so the sum of these positive terms is too, and its log
+# within ln(1 + 2^-8) = 3.9e-3 nats of the exact one.  A row dominated by one
+# p that is not exactly 1 (its max past the softmax reference) reaches that.
+BF16_LSE_ATOL = 4e-3
+
+
 def tolerances(w):
     """(max-abs, mean-abs, LSE atol) against the float64 oracle: the bf16
     bounds above for bf16 inputs; float32 inputs run float32 products and
     softmax, whose rounding (logits of magnitude <= 30 at 2^-24 relative,
     one-ulp exponentials) stays far below 1e-5.  The LSE also has a relative
     part (see _check_out)."""
-    return (MAX_ABS, MEAN_ABS, 2e-3) if w.dtype == "bf16" else (1e-5, 1e-6, 1e-5)
+    return (MAX_ABS, MEAN_ABS, BF16_LSE_ATOL) if w.dtype == "bf16" else (1e-5, 1e-6, 1e-5)
 
 
 def _say(msg):
